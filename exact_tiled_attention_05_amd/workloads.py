@@ -1,0 +1,102 @@
+"""Seeded synthetic workloads for the attention forward pass.
+
+This module only draws random numbers and shapes them; it holds none of the attention
+arithmetic, so both the GPU path's tests/bench and the CPU oracle can take their inputs from it.
+
+Recipe (shared by every workload):
+  * a CPU ``torch.Generator`` seeded with the workload's seed;
+  * Q, then K, then V drawn in that order as float32 standard normals of shape [B, H, N, d];
+  * workload-specific shaping (below), applied in float32;
+  * a cast to the compute dtype (bf16 or fp32). The cast tensors are what the GPU receives, and
+    the oracle upcasts exactly those tensors to float64.
+
+The five workloads are the shapes the pages discuss: a single small head, a mid-size batch at
+d = 64, the Llama-3-8B layer shape (32 heads at N = 8192, d = 128, causal) that the
+"FlashAttention-2 -- Deeper Math" page uses for its occupancy argument (Fix 4) and that
+"Flash Attention" ("The problem, quantified") uses for its traffic count, a large-score stress
+case, and a 32K-token causal case.
+"""
+import math
+
+import torch
+
+# name -> shape and recipe. "causal" lists the mask settings the workload is run with.
+WORKLOADS = {
+    "single_head_fp32": dict(B=1, H=1, N=256, d=64, dtype="fp32", causal=(False, True), seed=0),
+    "b4h16_n1k_d64": dict(B=4, H=16, N=1024, d=64, dtype="bf16", causal=(False,), seed=1),
+    "llama3_8b_n8k_causal": dict(B=1, H=32, N=8192, d=128, dtype="bf16", causal=(True,), seed=2),
+    "outlier_b16h32_n2k": dict(B=16, H=32, N=2048, d=128, dtype="bf16", causal=(False,), seed=3,
+                               q_mult=8.0, outlier_frac=0.01, outlier_mult=4.0),
+    "long_n32k_causal": dict(B=1, H=32, N=32768, d=128, dtype="bf16", causal=(True,), seed=4,
+                             sample_rows=64),
+}
+
+_TORCH_DTYPE = {"bf16": torch.bfloat16, "fp32": torch.float32}
+
+
+def softmax_scale(d):
+    """The conventional 1/sqrt(d), rounded once to float32 (the value both sides use)."""
+    return float(torch.tensor(1.0 / math.sqrt(d), dtype=torch.float32))
+
+
+def outlier_rows(N, count, seed):
+    """Indices of the key rows to enlarge in the large-score stress workload.
+
+    ``count`` distinct rows drawn with a seeded permutation; the last key (N-1) is always one of
+    them, so a late-arriving maximum is guaranteed whatever the key tile size, and at least one
+    more lands in the last tenth of the keys.
+    """
+    g = torch.Generator().manual_seed(seed)
+    perm = torch.randperm(N, generator=g)
+    chosen = [int(x) for x in perm[: max(count, 2)]]
+    if N - 1 not in chosen:
+        chosen[0] = N - 1
+    tail0 = N - max(1, N // 10)
+    if not any(tail0 <= c < N - 1 for c in chosen) and N >= 3:
+        chosen[1] = tail0 if tail0 != N - 1 else N - 2
+    return sorted(set(chosen))
+
+
+def make_inputs(B, H, N, d, dtype="bf16", seed=0, q_mult=1.0, outlier_frac=0.0,
+                outlier_mult=4.0, **_ignored):
+    """Return (q, k, v) CPU tensors of shape [B, H, N, d] in the compute dtype."""
+    g = torch.Generator().manual_seed(seed)
+    q = torch.randn((B, H, N, d), generator=g, dtype=torch.float32)
+    k = torch.randn((B, H, N, d), generator=g, dtype=torch.float32)
+    v = torch.randn((B, H, N, d), generator=g, dtype=torch.float32)
+    if q_mult != 1.0:
+        q.mul_(q_mult)
+    if outlier_frac > 0.0:
+        count = max(1, int(math.floor(outlier_frac * N)))
+        for b in range(B):
+            for h in range(H):
+                idx = outlier_rows(N, count, seed * 1000003 + b * 4099 + h)
+                k[b, h, idx] *= outlier_mult
+    t = _TORCH_DTYPE[dtype]
+    return q.to(t).contiguous(), k.to(t).contiguous(), v.to(t).contiguous()
+
+
+def sampled_rows(N, count, seed):
+    """Query rows checked against the oracle when the full output is too large to check.
+
+    Always includes the first and the last row; the rest are distinct rows drawn uniformly
+    with a seeded permutation. Returned sorted.
+    """
+    if count >= N:
+        return torch.arange(N)
+    g = torch.Generator().manual_seed(seed)
+    rest = torch.randperm(N - 2, generator=g)[: count - 2] + 1
+    return torch.sort(torch.cat([torch.tensor([0, N - 1]), rest])).values
+
+
+def workload_inputs(name):
+    """(q, k, v, scale) for a named workload."""
+    w = WORKLOADS[name]
+    q, k, v = make_inputs(**w)
+    return q, k, v, softmax_scale(w["d"])
+
+
+def metric_flops(B, H, N, d, causal):
+    """The throughput metric's FLOP count: 4*B*H*N^2*d, halved when causal."""
+    f = 4.0 * B * H * N * N * d
+    return f / 2.0 if causal else f

@@ -1,0 +1,20 @@
+"""CPU float64 oracle for exact scaled dot-product attention -- TEST INFRASTRUCTURE ONLY.
+
+Only ``tests/``, ``__graft_entry__.smoke()`` and the ``cpu_baseline`` leg of ``bench.py`` may
+import anything from this package. The product path (``exact_tiled_attention_05_amd``) never
+imports it, links it or falls back to it, and the oracle shares no code with the GPU path.
+
+Contents
+--------
+attention.py  -- the plain definition: materialise S = scale * Q K^T, mask, stable softmax,
+                 O = P V and LSE = m + ln(l), in float64, one (batch, head) at a time.
+online.py     -- the pages' streaming recurrences (online normaliser, blockwise (m, l, a)
+                 merge, tiled forward with queries outermost). A test model only: it is pinned
+                 to attention.py, it is not what the GPU is compared against.
+
+Every function is pinned by ``tests/test_oracle.py`` and ``tests/test_online_model.py`` to
+something other than itself: the worked example printed on the pages, closed forms,
+invariants, brute force in scalar Python, and float64 library routines.
+"""
+from .attention import attention, attention_head, dense_scores  # noqa: F401
+from .online import online_normalizer, blockwise_row, tiled_attention  # noqa: F401

@@ -1,0 +1,94 @@
+"""Dense CPU float64 attention: the definition the tiled GPU kernel must reproduce.
+
+TEST INFRASTRUCTURE ONLY -- imported by tests, the smoke check and the bench's cpu_baseline leg,
+never by the product path.
+
+What is computed (per batch b and head h, each an independent [N, d] problem):
+
+    S   = scale * Q K^T                        ("Understanding FlashAttention Pt 1", §0.2 and §1.2;
+                                                "Online Softmax & FlashAttention", Listing 26.2)
+    S[i, j] = -inf  for j > i  when causal      (same chapter, Listing 26.2's mask; handbook §3.5)
+    m   = max_j S[i, j]                         (stable softmax: handbook §2.2, chapter Eq 26.1)
+    E   = exp(S - m),  l = sum_j E[i, j]
+    P   = E / l,  O = P V
+    LSE = m + ln(l)                             ("FlashAttention-2 -- Deeper Math", Fix 2)
+
+S and P are materialised on purpose: this is the "standard attention" the pages contrast the
+tiled kernel with, and the tiled kernel is exact with respect to it up to rounding order
+("Flash Attention", introduction; handbook §3.2).
+
+Readings where the pages leave a choice open:
+  * ``scale`` is passed explicitly (the pages use 1/sqrt(d)); it multiplies q.k in float64.
+  * LSE is the natural log of the normaliser of the *scaled* scores, one value per query row.
+  * The inputs are upcast from exactly the tensors the GPU receives (bf16 or fp32), so the
+    only differences measured are the kernel's own arithmetic.
+  * A row with no visible key has no softmax; with N_q = N_k and the j <= i rule that cannot
+    happen, and the oracle raises if it would.
+"""
+import numpy as np
+
+
+def dense_scores(q, k, scale, causal, rows):
+    """S = scale * q[rows] k^T with the causal rule applied (future keys -> -inf).
+
+    q: [Nq, d], k: [N, d] float64; rows: int array of query indices into q.
+    Returns S: [len(rows), N] float64.
+    """
+    s = float(scale) * (q[rows] @ k.T)
+    if causal:
+        key_pos = np.arange(k.shape[0])[None, :]
+        qry_pos = np.asarray(rows)[:, None]
+        s = np.where(key_pos <= qry_pos, s, -np.inf)
+    return s
+
+
+def attention_head(q, k, v, scale, causal=False, rows=None, return_sp=False):
+    """One head of naive attention in float64.
+
+    q: [N, d], k: [N, d], v: [N, dv] (any float dtype; upcast to float64).
+    rows: optional sequence of query indices to evaluate (default: all N rows). Only those
+          rows of S are formed, each against every key.
+    Returns (O [R, dv], LSE [R]) and, if return_sp, also (S [R, N], P [R, N]).
+    """
+    q = np.asarray(q, dtype=np.float64)
+    k = np.asarray(k, dtype=np.float64)
+    v = np.asarray(v, dtype=np.float64)
+    if rows is None:
+        rows = np.arange(q.shape[0])
+    rows = np.asarray(rows, dtype=np.int64)
+    s = dense_scores(q, k, scale, causal, rows)
+    m = s.max(axis=1)
+    if not np.all(np.isfinite(m)):
+        raise ValueError("a query row has no visible key; its softmax is undefined")
+    e = np.exp(s - m[:, None])
+    ell = e.sum(axis=1)
+    p = e / ell[:, None]
+    o = p @ v
+    lse = m + np.log(ell)
+    if return_sp:
+        return o, lse, s, p
+    return o, lse
+
+
+def attention(q, k, v, scale, causal=False, rows=None):
+    """Batched naive attention over [B, H, N, d] arrays (numpy or anything np.asarray accepts).
+
+    rows: optional per-head query rows, either one index array used for every (b, h) or an
+          array of shape [B, H, R]. Returns (O [B, H, R, dv], LSE [B, H, R]) in float64.
+    """
+    q = np.asarray(q)
+    k = np.asarray(k)
+    v = np.asarray(v)
+    B, H = q.shape[0], q.shape[1]
+    R = q.shape[2] if rows is None else np.asarray(rows).shape[-1]
+    o = np.empty((B, H, R, v.shape[3]), dtype=np.float64)
+    lse = np.empty((B, H, R), dtype=np.float64)
+    for b in range(B):
+        for h in range(H):
+            if rows is None:
+                r = None
+            else:
+                ra = np.asarray(rows)
+                r = ra if ra.ndim == 1 else ra[b, h]
+            o[b, h], lse[b, h] = attention_head(q[b, h], k[b, h], v[b, h], scale, causal, r)
+    return o, lse
