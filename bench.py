@@ -1,0 +1,142 @@
+#!/usr/bin/env python3
+"""Throughput of the exact tiled attention forward pass on one MI355X.
+
+One step = one fa_fwd call over the whole workload (grid, Q load, K/V streaming, both MFMA
+contractions, online softmax, epilogue), with Q, K, V already resident in HBM. The default
+workload is the Llama-3-8B layer shape: B=1, H=32, N=8192, d=128, bf16, causal.
+
+Prints one JSON line:
+  value      = metric FLOPs (4*B*H*N^2*d, halved when causal) / mean step time, in TFLOP/s
+  roofline   = the kernel's achieved TFLOP/s against the dense bf16 MFMA peak, timed with HIP
+               events on the stream the kernel is launched on
+  cpu_baseline = the CPU float64 oracle timed on this host on a bounded sample of the workload
+
+Usage: python bench.py [--gpus 1] [--steps K] [--warmup W] [--workload NAME] [--no-cpu]
+"""
+import argparse
+import json
+import os
+import sys
+import time
+
+ROOT = os.path.dirname(os.path.abspath(__file__))
+sys.path.insert(0, ROOT)
+
+PEAK_BF16_TFLOPS = 2516.6  # MI355X dense bf16 MFMA: 256 CU x 2.4 GHz x 4096 FLOP/clk
+PEAK_F32_TFLOPS = 157.3    # MI355X fp32 vector
+
+
+def parse():
+    ap = argparse.ArgumentParser()
+    ap.add_argument("--gpus", type=int, default=1)
+    ap.add_argument("--steps", type=int, default=50)
+    ap.add_argument("--warmup", type=int, default=10)
+    ap.add_argument("--workload", default="llama3_8b_n8k_causal")
+    ap.add_argument("--no-cpu", action="store_true", help="skip the cpu_baseline leg")
+    ap.add_argument("--cpu-heads", type=int, default=0,
+                    help="heads in the cpu_baseline sample (0 = pick for ~10-30 s)")
+    return ap.parse_args()
+
+
+def cpu_baseline(q, k, v, scale, causal, w, n_heads):
+    """Time the float64 oracle, as it stands, on the first n_heads heads (all their rows)."""
+    import numpy as np
+    from oracle import attention_head
+    try:
+        from threadpoolctl import threadpool_info
+        threads = max([i.get("num_threads", 1) for i in threadpool_info()
+                       if i.get("user_api") == "blas"] or [1])
+    except Exception:  # pragma: no cover
+        threads = 1
+    heads = [(b, h) for b in range(w["B"]) for h in range(w["H"])][:n_heads]
+    arrays = [tuple(x[b, h].float().numpy().astype(np.float64) for x in (q, k, v))
+              for b, h in heads]
+    t0 = time.perf_counter()
+    for qh, kh, vh in arrays:
+        attention_head(qh, kh, vh, scale, causal)
+    dt = time.perf_counter() - t0
+    from exact_tiled_attention_05_amd.workloads import metric_flops
+    flops = metric_flops(1, len(heads), w["N"], w["d"], causal)
+    return {"value": flops / dt / 1e12, "unit": "TFLOP/s", "cores": threads, "kind": "oracle",
+            "sample": "%d of %d heads, every row (numpy float64, dense S and P), %.1f s"
+                      % (len(heads), w["B"] * w["H"], dt)}
+
+
+def main():
+    args = parse()
+    if args.gpus != 1:
+        print("bench.py: this build runs on exactly one GPU (no multi-GPU path); "
+              "run with --gpus 1", file=sys.stderr)
+        sys.exit(2)
+
+    import torch
+    import exact_tiled_attention_05_amd as fa
+    from exact_tiled_attention_05_amd import workloads as W
+
+    w = W.WORKLOADS[args.workload]
+    causal = w["causal"][-1]
+    q, k, v, scale = W.workload_inputs(args.workload)
+    dev = torch.device("cuda:0")
+    qd, kd, vd = (x.to(dev) for x in (q, k, v))
+    o = torch.empty_like(qd)
+    lse = torch.empty((w["B"], w["H"], w["N"]), dtype=torch.float32, device=dev)
+    stream = torch.cuda.current_stream(dev)
+    fn = fa.fa_fwd if w["dtype"] == "bf16" else fa.fa_fwd_f32
+    argv = (qd.data_ptr(), kd.data_ptr(), vd.data_ptr(), o.data_ptr(), lse.data_ptr(),
+            w["B"], w["H"], w["N"], w["d"], scale, int(causal), stream.cuda_stream)
+
+    def step():
+        rc = fn(*argv)
+        if rc != fa.FA_OK:
+            raise fa.FAError(rc, fn.__name__)
+
+    for _ in range(args.warmup):
+        step()
+    torch.cuda.synchronize()
+
+    # Events are recorded on the stream the kernels are launched on.
+    e0 = torch.cuda.Event(enable_timing=True)
+    e1 = torch.cuda.Event(enable_timing=True)
+    torch.cuda.synchronize()
+    t0 = time.perf_counter()
+    e0.record(stream)
+    for _ in range(args.steps):
+        step()
+    e1.record(stream)
+    torch.cuda.synchronize()
+    wall = time.perf_counter() - t0
+    ms = e0.elapsed_time(e1) / args.steps
+
+    flops = W.metric_flops(w["B"], w["H"], w["N"], w["d"], causal)
+    tflops = flops / (ms * 1e-3) / 1e12
+    peak = PEAK_BF16_TFLOPS if w["dtype"] == "bf16" else PEAK_F32_TFLOPS
+
+    rec = {
+        "metric": "attention fwd TFLOP/s (4*B*H*N^2*d, 1/2 if causal)",
+        "value": round(tflops, 2),
+        "unit": "TFLOP/s",
+        "n_gpus": 1,
+        "steps": args.steps,
+        "warmup": args.warmup,
+        "ms_per_step": round(ms, 5),
+        "higher_is_better": True,
+        "scaling": "weak",
+        "vs_baseline": None,
+        "dtype": w["dtype"],
+        "data": "synthetic (seeded N(0,1) Q, K, V)",
+        "config": {"workload": args.workload, "B": w["B"], "H": w["H"], "N": w["N"],
+                   "d": w["d"], "causal": causal, "kernel": "fa_fwd" if w["dtype"] == "bf16"
+                   else "fa_fwd_f32"},
+        "roofline": {"bound": "mfma" if w["dtype"] == "bf16" else "alu",
+                     "achieved": round(tflops, 2), "peak": peak, "unit": "TFLOP/s",
+                     "frac": round(tflops / peak, 4), "traffic": None},
+        "wall_s_timed_region": round(wall, 4),
+    }
+    if not args.no_cpu:
+        n_heads = args.cpu_heads or max(1, min(w["B"] * w["H"], int(4 * (8192 / w["N"]) ** 2)))
+        rec["cpu_baseline"] = cpu_baseline(q, k, v, scale, causal, w, n_heads)
+    print(json.dumps(rec), flush=True)
+
+
+if __name__ == "__main__":
+    main()

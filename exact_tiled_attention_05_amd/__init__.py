@@ -1,0 +1,120 @@
+"""Exact tiled attention forward pass for AMD MI355X (gfx950): Python binding of ``libfa.so``.
+
+The library computes, per batch and head, O = softmax(scale * Q K^T [causal mask]) V and the
+per-row logsumexp, tile by tile, without ever writing the N x N score matrix (see
+``include/fa.h`` for the full contract). This module only marshals arguments: every step of the
+computation runs in the HIP kernels of ``libfa.so``. There is no CPU fallback; if the library
+is missing the calls raise.
+
+Raw entry points (same names and argument order as the C-ABI; pointers are integers):
+    fa_fwd(q, k, v, o, lse, B, H, N, d, scale, causal, stream) -> int
+    fa_fwd_f32(q, k, v, o, lse, B, H, N, d, scale, causal, stream) -> int
+    fa_strerror(code) -> str
+    fa_version() -> int
+Tensor convenience (PyTorch supplies device memory and the stream):
+    forward(q, k, v, scale=None, causal=False, out=None, lse=None) -> (o, lse)
+"""
+import ctypes
+import math
+import os
+
+__all__ = ["fa_fwd", "fa_fwd_f32", "fa_strerror", "fa_version", "forward", "FAError",
+           "library_path", "load_library", "FA_OK", "FA_ERR_INVALID_ARG", "FA_ERR_UNSUPPORTED",
+           "FA_ERR_ALIGNMENT", "FA_ERR_LAUNCH"]
+
+FA_OK = 0
+FA_ERR_INVALID_ARG = -1
+FA_ERR_UNSUPPORTED = -2
+FA_ERR_ALIGNMENT = -3
+FA_ERR_LAUNCH = -4
+
+_HERE = os.path.dirname(os.path.abspath(__file__))
+_LIB = None
+
+
+def library_path():
+    return os.path.join(_HERE, "libfa.so")
+
+
+class FAError(RuntimeError):
+    def __init__(self, code, where):
+        self.code = code
+        super().__init__("%s failed: %s (code %d)" % (where, fa_strerror(code), code))
+
+
+def load_library():
+    """Load libfa.so from the package directory (built by ``exact_tiled_attention_05_amd.build``)."""
+    global _LIB
+    if _LIB is None:
+        path = library_path()
+        if not os.path.exists(path):
+            raise RuntimeError("libfa.so is not built (expected at %s); run "
+                               "`python -m exact_tiled_attention_05_amd.build`" % path)
+        lib = ctypes.CDLL(path)
+        fwd_args = [ctypes.c_void_p] * 5 + [ctypes.c_int] * 4 + [ctypes.c_float, ctypes.c_int,
+                                                                   ctypes.c_void_p]
+        for name in ("fa_fwd", "fa_fwd_f32"):
+            fn = getattr(lib, name)
+            fn.argtypes = fwd_args
+            fn.restype = ctypes.c_int
+        lib.fa_strerror.argtypes = [ctypes.c_int]
+        lib.fa_strerror.restype = ctypes.c_char_p
+        lib.fa_version.argtypes = []
+        lib.fa_version.restype = ctypes.c_int
+        _LIB = lib
+    return _LIB
+
+
+def fa_fwd(q, k, v, o, lse, B, H, N, d, scale, causal, stream=None):
+    return load_library().fa_fwd(q, k, v, o, lse, B, H, N, d, scale, causal, stream)
+
+
+def fa_fwd_f32(q, k, v, o, lse, B, H, N, d, scale, causal, stream=None):
+    return load_library().fa_fwd_f32(q, k, v, o, lse, B, H, N, d, scale, causal, stream)
+
+
+def fa_strerror(code):
+    return load_library().fa_strerror(code).decode()
+
+
+def fa_version():
+    return load_library().fa_version()
+
+
+def forward(q, k, v, scale=None, causal=False, out=None, lse=None, stream=None):
+    """Attention forward on [B, H, N, d] CUDA/HIP tensors (bf16 or fp32, contiguous).
+
+    Returns (o, lse) with o like q and lse float32 [B, H, N]. ``out``/``lse`` may be passed to
+    reuse buffers; ``stream`` defaults to torch's current stream on q's device.
+    """
+    import torch
+
+    if q.dim() != 4 or k.shape != q.shape or v.shape != q.shape:
+        raise ValueError("q, k, v must all be [B, H, N, d] with the same shape")
+    if not (q.dtype == k.dtype == v.dtype) or q.dtype not in (torch.bfloat16, torch.float32):
+        raise ValueError("q, k, v must all be bfloat16 or all float32")
+    if not (q.is_cuda and k.device == q.device and v.device == q.device):
+        raise ValueError("q, k, v must be on the same GPU device")
+    if not (q.is_contiguous() and k.is_contiguous() and v.is_contiguous()):
+        raise ValueError("q, k, v must be contiguous")
+    B, H, N, d = q.shape
+    if scale is None:
+        scale = 1.0 / math.sqrt(d)
+    if out is None:
+        out = torch.empty_like(q)
+    if lse is None:
+        lse = torch.empty((B, H, N), dtype=torch.float32, device=q.device)
+    if (out.shape != q.shape or out.dtype != q.dtype or not out.is_contiguous()
+            or out.device != q.device):
+        raise ValueError("out must be a contiguous tensor like q")
+    if (tuple(lse.shape) != (B, H, N) or lse.dtype != torch.float32 or not lse.is_contiguous()
+            or lse.device != q.device):
+        raise ValueError("lse must be a contiguous float32 [B, H, N] tensor on q's device")
+    if stream is None:
+        stream = torch.cuda.current_stream(q.device).cuda_stream
+    fn = fa_fwd if q.dtype == torch.bfloat16 else fa_fwd_f32
+    rc = fn(q.data_ptr(), k.data_ptr(), v.data_ptr(), out.data_ptr(), lse.data_ptr(),
+            B, H, N, d, float(scale), int(bool(causal)), stream)
+    if rc != FA_OK:
+        raise FAError(rc, fn.__name__)
+    return out, lse

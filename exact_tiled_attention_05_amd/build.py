@@ -1,0 +1,47 @@
+"""Build libfa.so (the C-ABI attention library) in-tree with hipcc for gfx950.
+
+Usage: ``python -m exact_tiled_attention_05_amd.build`` or ``build()`` from Python. The library
+lands next to this file, where the Python binding loads it from.
+"""
+import os
+import subprocess
+import sys
+
+PKG_DIR = os.path.dirname(os.path.abspath(__file__))
+ROOT = os.path.dirname(PKG_DIR)
+CSRC = os.path.join(PKG_DIR, "csrc")
+INCLUDE = os.path.join(ROOT, "include")
+LIB_PATH = os.path.join(PKG_DIR, "libfa.so")
+
+# Packed fp32 VALU instructions are disabled for all device code.
+HIP_FLAGS = [
+    "--offload-arch=gfx950", "-O3", "-std=c++17", "-fPIC", "-shared",
+    "-Xclang", "-target-feature", "-Xclang", "-packed-fp32-ops",
+    "-Wall", "-Wno-unused-result",
+]
+
+
+def hipcc_path():
+    return os.environ.get("HIPCC", "/opt/rocm/bin/hipcc")
+
+
+def build(verbose=False, extra_flags=(), out=LIB_PATH):
+    """Compile csrc/fa_api.hip (which includes the kernels) into ``out``; returns its path."""
+    tmp = out + ".tmp%d" % os.getpid()
+    cmd = [hipcc_path()] + HIP_FLAGS + list(extra_flags) + [
+        "-I", INCLUDE, "-I", CSRC, os.path.join(CSRC, "fa_api.hip"), "-o", tmp]
+    if verbose:
+        print(" ".join(cmd), flush=True)
+    r = subprocess.run(cmd, stdout=subprocess.PIPE, stderr=subprocess.STDOUT, text=True)
+    # hipcc's host pass does not know the device-only feature flag; that warning is harmless.
+    msgs = [ln for ln in r.stdout.splitlines() if "packed-fp32-ops" not in ln]
+    if r.returncode != 0:
+        raise RuntimeError("hipcc failed (%d):\n%s" % (r.returncode, "\n".join(msgs)))
+    if verbose and msgs:
+        print("\n".join(msgs), flush=True)
+    os.replace(tmp, out)
+    return out
+
+
+if __name__ == "__main__":
+    print(build(verbose="-v" in sys.argv))

@@ -1,0 +1,81 @@
+/*
+ * fa.h -- exact tiled attention forward pass (FlashAttention-style) for AMD MI355X (gfx950).
+ *
+ * The operation. For every batch b and head h independently, with Q, K, V the [N, d] slices:
+ *
+ *     S   = scale * Q K^T                      (a score per query i and key j)
+ *     S[i][j] = -inf for j > i   when causal   (a query sees itself and earlier keys only)
+ *     O   = softmax_rows(S) V                  (stable softmax: exponentials taken relative
+ *                                               to the row maximum m, normalised by their sum l)
+ *     LSE = m + ln(l)                          (one float per query row)
+ *
+ * This is ordinary scaled dot-product attention ("Understanding FlashAttention Pt 1", §0.2 and
+ * §1.2; "Online Softmax & FlashAttention", Eq 26.1 and Listing 26.2). The library computes it
+ * tile by tile with a running maximum, a running sum and an unnormalised accumulator that is
+ * rescaled whenever the reference maximum moves, divides by the sum once after the last key
+ * tile, and writes the logsumexp per row ("FlashAttention-2 -- Deeper Math", Fixes 1-5 and
+ * "Causal masking: skip the blocks"). The N x N matrices S and P are never written to memory.
+ * The result is exact up to floating-point rounding order; it is not an approximation.
+ *
+ * Conventions shared by every entry point:
+ *   - q, k, v, o, lse are DEVICE pointers owned by the caller. The library never allocates,
+ *     frees, copies or synchronises; it only enqueues kernels on `stream`.
+ *   - Layout: contiguous row-major [B][H][N][d] for q, k, v and o; contiguous [B][H][N] for lse.
+ *     Self-attention only: queries and keys have the same length N, and V has head dim d.
+ *   - scale multiplies q.k in fp32 before the softmax (pass 1/sqrt(d) for the usual attention).
+ *     It must be finite and >= 0.
+ *   - causal is 0 (every query sees every key) or 1 (query i sees keys 0..i).
+ *   - lse holds ln(sum_j exp(S[i][j] - m_i)) + m_i of the scaled scores, in natural-log units.
+ *   - o must not overlap q, k, v or lse; lse must not overlap q, k, v or o.
+ *   - stream is a hipStream_t (NULL = the default stream). The call is asynchronous: errors in
+ *     argument checking are returned before any HIP call is made; a launch failure is reported
+ *     as FA_ERR_LAUNCH (the launch call's own status).
+ *   - Deterministic: the same inputs give bitwise-identical outputs run to run (no atomics, no
+ *     cross-workgroup reductions).
+ *   - Thread-safe: no global mutable state.
+ *   - Limits: 1 <= N <= 2^22 and 1 <= B*H <= 65535.
+ */
+#ifndef FA_H_
+#define FA_H_
+
+#ifdef __cplusplus
+extern "C" {
+#endif
+
+#define FA_OK 0
+#define FA_ERR_INVALID_ARG (-1) /* null pointer, B/H/N out of range, causal not 0/1, scale
+                                   negative or not finite, or overlapping output buffers */
+#define FA_ERR_UNSUPPORTED (-2) /* head dim d not in {64, 128} */
+#define FA_ERR_ALIGNMENT (-3)   /* a pointer is not 16-byte aligned */
+#define FA_ERR_LAUNCH (-4)      /* the kernel launch call returned an error */
+
+/*
+ * fa_fwd -- bf16 inputs and outputs, fp32 arithmetic for the softmax and both accumulations.
+ *   q, k, v : const bf16 (bfloat16, 2 bytes) [B][H][N][d]
+ *   o       : bf16 [B][H][N][d], written (rounded to nearest even from fp32)
+ *   lse     : float [B][H][N], written
+ * The two contractions Q K^T and P V run on bf16 matrix cores with fp32 accumulation; P is
+ * rounded to bf16 (nearest even) before P V, and the row sum l is taken from the fp32 P.
+ * Returns FA_OK or one of the FA_ERR_* codes above.
+ */
+int fa_fwd(const void* q, const void* k, const void* v, void* o, float* lse,
+           int B, int H, int N, int d, float scale, int causal, void* stream);
+
+/*
+ * fa_fwd_f32 -- fp32 inputs and outputs; every step in fp32 (no bf16 or reduced-precision
+ * matrix arithmetic anywhere). Same layout, conventions and return codes as fa_fwd.
+ */
+int fa_fwd_f32(const float* q, const float* k, const float* v, float* o, float* lse,
+               int B, int H, int N, int d, float scale, int causal, void* stream);
+
+/* Human-readable text for a return code (static storage; never NULL). */
+const char* fa_strerror(int code);
+
+/* Library version as major*10000 + minor*100 + patch. */
+int fa_version(void);
+
+#ifdef __cplusplus
+}
+#endif
+
+#endif /* FA_H_ */

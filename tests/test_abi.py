@@ -1,0 +1,106 @@
+"""The C-ABI boundary on the CPU: libfa.so loads, exports every function include/fa.h declares,
+and refuses bad arguments with the documented codes before making any HIP call (no compute runs
+here; the pointers below are never dereferenced)."""
+import ctypes
+import os
+import re
+
+import pytest
+import torch
+
+import exact_tiled_attention_05_amd as fa
+
+ROOT = os.path.dirname(os.path.dirname(os.path.abspath(__file__)))
+HEADER = os.path.join(ROOT, "include", "fa.h")
+
+
+def _declared():
+    text = open(HEADER).read()
+    text = re.sub(r"/\*.*?\*/", "", text, flags=re.S)
+    return sorted(set(re.findall(r"\b(fa_[a-z0-9_]+)\s*\(", text)))
+
+
+def _codes():
+    text = open(HEADER).read()
+    return {m[0]: int(m[1]) for m in re.findall(r"#define\s+(FA_[A-Z_]+)\s+\(?(-?\d+)\)?", text)}
+
+
+def test_header_declares_the_expected_entry_points():
+    assert _declared() == ["fa_fwd", "fa_fwd_f32", "fa_strerror", "fa_version"]
+
+
+def test_library_exports_every_declared_symbol():
+    lib = ctypes.CDLL(fa.library_path())
+    for name in _declared():
+        assert hasattr(lib, name), name
+
+
+def test_python_codes_match_header():
+    for name, value in _codes().items():
+        assert getattr(fa, name) == value, name
+
+
+def test_version_and_strerror():
+    assert fa.fa_version() >= 100
+    for code in (0, -1, -2, -3, -4):
+        assert fa.fa_strerror(code) and fa.fa_strerror(code) != "unknown error code"
+    assert fa.fa_strerror(12345) == "unknown error code"
+
+
+# Fake, 16-byte aligned, non-overlapping "device" addresses. Every call below fails validation,
+# which happens before any HIP call, so they are never dereferenced.
+A = 1 << 40
+Q, K, V, O, L = (A + i * (1 << 32) for i in range(5))
+GOOD = dict(q=Q, k=K, v=V, o=O, lse=L, B=2, H=3, N=100, d=64, scale=0.125, causal=0)
+
+
+def _call(fn, **kw):
+    a = dict(GOOD, **kw)
+    return fn(a["q"], a["k"], a["v"], a["o"], a["lse"], a["B"], a["H"], a["N"], a["d"],
+              a["scale"], a["causal"], None)
+
+
+BAD = [
+    (dict(q=0), fa.FA_ERR_INVALID_ARG),
+    (dict(k=0), fa.FA_ERR_INVALID_ARG),
+    (dict(v=0), fa.FA_ERR_INVALID_ARG),
+    (dict(o=0), fa.FA_ERR_INVALID_ARG),
+    (dict(lse=0), fa.FA_ERR_INVALID_ARG),
+    (dict(B=0), fa.FA_ERR_INVALID_ARG),
+    (dict(H=-1), fa.FA_ERR_INVALID_ARG),
+    (dict(N=0), fa.FA_ERR_INVALID_ARG),
+    (dict(N=(1 << 22) + 1), fa.FA_ERR_INVALID_ARG),
+    (dict(B=256, H=256), fa.FA_ERR_INVALID_ARG),
+    (dict(causal=2), fa.FA_ERR_INVALID_ARG),
+    (dict(causal=-1), fa.FA_ERR_INVALID_ARG),
+    (dict(scale=-0.5), fa.FA_ERR_INVALID_ARG),
+    (dict(scale=float("inf")), fa.FA_ERR_INVALID_ARG),
+    (dict(scale=float("nan")), fa.FA_ERR_INVALID_ARG),
+    (dict(d=96), fa.FA_ERR_UNSUPPORTED),
+    (dict(d=256), fa.FA_ERR_UNSUPPORTED),
+    (dict(d=0), fa.FA_ERR_UNSUPPORTED),
+    (dict(q=Q + 8), fa.FA_ERR_ALIGNMENT),
+    (dict(lse=L + 4), fa.FA_ERR_ALIGNMENT),
+    (dict(o=Q), fa.FA_ERR_INVALID_ARG),            # o aliases q
+    (dict(o=K + 16), fa.FA_ERR_INVALID_ARG),       # o overlaps k
+    (dict(lse=O + 1024), fa.FA_ERR_INVALID_ARG),   # lse inside o
+    (dict(lse=V), fa.FA_ERR_INVALID_ARG),          # lse aliases v
+]
+
+
+@pytest.mark.parametrize("fn_name", ["fa_fwd", "fa_fwd_f32"])
+@pytest.mark.parametrize("kw,code", BAD, ids=[str(b[0]) for b in BAD])
+def test_bad_arguments_are_refused(fn_name, kw, code):
+    assert _call(getattr(fa, fn_name), **kw) == code
+
+
+def test_forward_checks_tensors_before_any_gpu_use():
+    q = torch.zeros(1, 1, 8, 64, dtype=torch.bfloat16)
+    with pytest.raises(ValueError):
+        fa.forward(q, q, q)  # CPU tensors
+    with pytest.raises(ValueError):
+        fa.forward(q, q, q.float())  # mixed dtypes
+    with pytest.raises(ValueError):
+        fa.forward(q[0], q[0], q[0])  # not 4-D
+    with pytest.raises(ValueError):
+        fa.forward(q.half(), q.half(), q.half())  # fp16 is not a supported dtype
