@@ -34,12 +34,29 @@ def parse():
     ap.add_argument("--workload", default="llama3_8b_n8k_causal")
     ap.add_argument("--no-cpu", action="store_true", help="skip the cpu_baseline leg")
     ap.add_argument("--cpu-heads", type=int, default=0,
-                    help="heads in the cpu_baseline sample (0 = pick for ~10-30 s)")
+                    help="max heads in the cpu_baseline sample (0 = all, capped at ~15 s)")
+    ap.add_argument("--print-digest", action="store_true",
+                    help="print the kernel source digest that recorded counters are keyed to")
+    ap.add_argument("--copy-calib", type=int, default=0, metavar="BYTES",
+                    help="instead of attention, run --steps plain device copies of BYTES bytes "
+                         "(reference kernel for scaling the HBM byte counters)")
     return ap.parse_args()
 
 
-def cpu_baseline(q, k, v, scale, causal, w, n_heads):
-    """Time the float64 oracle, as it stands, on the first n_heads heads (all their rows)."""
+def copy_calibration(nbytes, steps):
+    """A plain device-to-device copy of known size: reads and writes nbytes per launch."""
+    import torch
+    src = torch.ones(nbytes // 4, dtype=torch.float32, device="cuda:0")
+    dst = torch.empty_like(src)
+    for _ in range(steps):
+        dst.copy_(src)
+    torch.cuda.synchronize()
+    print(json.dumps({"copy_bytes_per_launch": nbytes, "launches": steps}), flush=True)
+
+
+def cpu_baseline(q, k, v, scale, causal, w, n_heads, budget_s=15.0):
+    """Time the float64 oracle, as it stands, on whole heads (all their rows), in order, until
+    n_heads heads are done or budget_s seconds have passed (at least one head)."""
     import numpy as np
     from oracle import attention_head
     try:
@@ -49,17 +66,48 @@ def cpu_baseline(q, k, v, scale, causal, w, n_heads):
     except Exception:  # pragma: no cover
         threads = 1
     heads = [(b, h) for b in range(w["B"]) for h in range(w["H"])][:n_heads]
-    arrays = [tuple(x[b, h].float().numpy().astype(np.float64) for x in (q, k, v))
-              for b, h in heads]
-    t0 = time.perf_counter()
-    for qh, kh, vh in arrays:
+    dt = 0.0
+    done = 0
+    for b, h in heads:
+        qh, kh, vh = (x[b, h].float().numpy().astype(np.float64) for x in (q, k, v))
+        t0 = time.perf_counter()
         attention_head(qh, kh, vh, scale, causal)
-    dt = time.perf_counter() - t0
+        dt += time.perf_counter() - t0
+        done += 1
+        if dt >= budget_s:
+            break
     from exact_tiled_attention_05_amd.workloads import metric_flops
-    flops = metric_flops(1, len(heads), w["N"], w["d"], causal)
+    flops = metric_flops(1, done, w["N"], w["d"], causal)
     return {"value": flops / dt / 1e12, "unit": "TFLOP/s", "cores": threads, "kind": "oracle",
             "sample": "%d of %d heads, every row (numpy float64, dense S and P), %.1f s"
-                      % (len(heads), w["B"] * w["H"], dt)}
+                      % (done, w["B"] * w["H"], dt)}
+
+
+def kernel_source_digest():
+    """sha256 over the HIP sources and build flags of libfa.so (identifies the kernel build)."""
+    import hashlib
+    from exact_tiled_attention_05_amd import build as B
+    hsh = hashlib.sha256()
+    for d in (B.CSRC, B.INCLUDE):
+        for name in sorted(os.listdir(d)):
+            with open(os.path.join(d, name), "rb") as f:
+                hsh.update(name.encode() + b"\0" + f.read())
+    hsh.update(" ".join(B.HIP_FLAGS).encode())
+    return hsh.hexdigest()
+
+
+def recorded_traffic(workload):
+    """HBM bytes per launch recorded with rocprofv3 counters for this workload, if they were
+    taken on the current kernel sources (else None)."""
+    path = os.path.join(ROOT, "profiles", "traffic.json")
+    try:
+        with open(path) as f:
+            rec = json.load(f).get(workload)
+    except (OSError, ValueError):
+        return None
+    if not rec or rec.get("source_sha256") != kernel_source_digest():
+        return None
+    return rec.get("bytes_per_launch")
 
 
 def main():
@@ -68,6 +116,13 @@ def main():
         print("bench.py: this build runs on exactly one GPU (no multi-GPU path); "
               "run with --gpus 1", file=sys.stderr)
         sys.exit(2)
+
+    if args.print_digest:
+        print(kernel_source_digest())
+        return
+    if args.copy_calib:
+        copy_calibration(args.copy_calib, args.steps)
+        return
 
     import torch
     import exact_tiled_attention_05_amd as fa
@@ -129,11 +184,11 @@ def main():
                    else "fa_fwd_f32"},
         "roofline": {"bound": "mfma" if w["dtype"] == "bf16" else "alu",
                      "achieved": round(tflops, 2), "peak": peak, "unit": "TFLOP/s",
-                     "frac": round(tflops / peak, 4), "traffic": None},
+                     "frac": round(tflops / peak, 4), "traffic": recorded_traffic(args.workload)},
         "wall_s_timed_region": round(wall, 4),
     }
     if not args.no_cpu:
-        n_heads = args.cpu_heads or max(1, min(w["B"] * w["H"], int(4 * (8192 / w["N"]) ** 2)))
+        n_heads = args.cpu_heads or w["B"] * w["H"]
         rec["cpu_baseline"] = cpu_baseline(q, k, v, scale, causal, w, n_heads)
     print(json.dumps(rec), flush=True)
 

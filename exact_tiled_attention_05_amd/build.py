@@ -13,10 +13,12 @@ CSRC = os.path.join(PKG_DIR, "csrc")
 INCLUDE = os.path.join(ROOT, "include")
 LIB_PATH = os.path.join(PKG_DIR, "libfa.so")
 
-# Packed fp32 VALU instructions are disabled for all device code.
+# Packed fp32 VALU instructions are disabled for all device code. NaNs are never produced by the
+# kernels for finite inputs (hidden keys are -inf, never 0*inf), so max needs no NaN handling.
 HIP_FLAGS = [
     "--offload-arch=gfx950", "-O3", "-std=c++17", "-fPIC", "-shared",
     "-Xclang", "-target-feature", "-Xclang", "-packed-fp32-ops",
+    "-fno-honor-nans",
     "-Wall", "-Wno-unused-result",
 ]
 

@@ -2,6 +2,7 @@
 // Declared (with their contract) in include/fa.h.
 #include <hip/hip_runtime.h>
 
+#include <cfloat>
 #include <cmath>
 #include <cstdint>
 
@@ -16,9 +17,19 @@ constexpr int kMaxN = 1 << 22;
 constexpr int kMaxBH = 65535;  // grid y of the fp32 kernel; also keeps bf16 grids < 2^31
 
 // Kernel shape for the bf16 path: rows per wave = 32*QB, waves per workgroup = NW, key tile BC.
-constexpr int kQB = 2;
-constexpr int kNW = 4;
-constexpr int kBC = 64;
+// (Overridable at build time for tuning sweeps.)
+#ifndef FA_QB
+#define FA_QB 1
+#endif
+#ifndef FA_NW
+#define FA_NW 8
+#endif
+#ifndef FA_BC
+#define FA_BC 64
+#endif
+constexpr int kQB = FA_QB;
+constexpr int kNW = FA_NW;
+constexpr int kBC = FA_BC;
 
 bool ranges_overlap(const void* a, size_t na, const void* b, size_t nb) {
   const uintptr_t x = reinterpret_cast<uintptr_t>(a), y = reinterpret_cast<uintptr_t>(b);
@@ -79,7 +90,9 @@ int fa_fwd(const void* q, const void* k, const void* v, void* o, float* lse, int
   a.lse = lse;
   a.N = N;
   a.BH = B * H;
-  a.scale_log2 = scale * fa::kLog2e;
+  // scale 0 runs as the smallest normal float: every probability still rounds to exactly 1 (the
+  // scaled scores are below 2^-24 in magnitude), while hidden keys stay at -inf instead of 0*inf.
+  a.scale_log2 = scale > 0.f ? scale * fa::kLog2e : FLT_MIN;
   const hipStream_t s = static_cast<hipStream_t>(stream);
   hipError_t e;
   if (d == 128) {

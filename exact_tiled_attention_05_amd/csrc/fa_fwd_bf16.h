@@ -24,8 +24,11 @@
 //   * Lazy rescaling: the reference maximum only moves when a new score exceeds it by more than
 //     kRescaleSlack (log2 units); otherwise p <= 2^kRescaleSlack and the alpha multiply of the
 //     accumulator is skipped for the whole wave. Any reference gives the same real-arithmetic
-//     result (the rescale identity holds for every reference value), and the slack bounds p so
-//     fp32 accumulation cannot overflow.
+//     result (the rescale identity holds for every reference value). The slack is kept small (a
+//     factor 4): a score that arrives without a rescale keeps the key that set the reference at
+//     >= 1/5 of their combined weight, so the bf16 rounding of its p cannot dominate a row's
+//     output; a large slack (2^8) lets a dominant late key carry a full 2^-9 relative rounding
+//     error into O.
 //   * Causal: tiles above the diagonal are never loaded or computed; sub-blocks below it run
 //     without a mask; only sub-blocks crossing the diagonal (or the ragged tail) are masked.
 #pragma once
@@ -34,7 +37,12 @@
 
 namespace fa {
 
-constexpr float kRescaleSlack = 8.0f;
+constexpr float kRescaleSlack = 2.0f;
+
+// Tuning knob: request all K and V fragments of a 32-key sub-block ahead of their MFMAs.
+#ifndef FA_HOIST_LDS
+#define FA_HOIST_LDS 0
+#endif
 
 struct Bf16Args {
   const bf16* q;
@@ -87,7 +95,213 @@ struct RowState {
   float l[QB];         // this lane's part of the running sum (its 16 keys per 32-key block)
 };
 
-// Consume one [BC][D] K/V tile held in LDS: S^T = K Q^T, online softmax update, O^T += V^T P^T.
+// Tree reductions over the 16 values a lane holds for one 32x32 block (short dependency chains).
+__device__ __forceinline__ float max3(float a, float b, float c) {
+  return __builtin_fmaxf(__builtin_fmaxf(a, b), c);  // one v_max3_f32
+}
+__device__ __forceinline__ float max16(const f32x16& v) {
+  const float a = max3(v[0], v[1], v[2]), b = max3(v[3], v[4], v[5]);
+  const float c = max3(v[6], v[7], v[8]), d = max3(v[9], v[10], v[11]);
+  const float e = max3(v[12], v[13], v[14]);
+  return max3(max3(a, b, c), max3(d, e, v[15]), -INFINITY);
+}
+__device__ __forceinline__ float sum16(const float (&p)[16]) {
+  float t[8];
+#pragma unroll
+  for (int i = 0; i < 8; i++) t[i] = p[2 * i] + p[2 * i + 1];
+#pragma unroll
+  for (int i = 0; i < 4; i++) t[i] = t[2 * i] + t[2 * i + 1];
+  return (t[0] + t[1]) + (t[2] + t[3]);
+}
+
+// One 32-key sub-block: S^T = K Q^T, online softmax update, O^T += V^T P^T.
+// MASKED sub-blocks cross the causal diagonal or the ragged tail; their hidden scores become -inf
+// before the maximum, and exp2(-inf) = 0 removes them from the sums (scale_log2 is never 0 here:
+// the host runs scale 0 as the smallest normal float, which gives the same probabilities).
+#if FA_HOIST_LDS
+template <int D, bool CAUSAL, bool MASKED, int QB, int NW, int BC>
+__device__ __forceinline__ void consume_sub(const char* __restrict__ Kt,
+                                            const char* __restrict__ Vt, int sb, int kb0, int qw0,
+                                            int N, float scale_log2, int c, int h, int vrow,
+                                            int vcol, const bf16x8 (&qf)[QB][D / 16],
+                                            RowState<QB, D / 32>& st) {
+  using C = Bf16Cfg<D, QB, NW, BC>;
+  // S^T[key][query] for 32 keys x 32 queries per qb. All K fragments are requested before the
+  // first MFMA so that LDS latency overlaps the MFMA chain.
+  bf16x8 kf[C::DK];
+#pragma unroll
+  for (int dk = 0; dk < C::DK; dk++)
+    kf[dk] = lds_read_b128(Kt + tile_off<D>(32 * sb + c, 16 * dk + 8 * h));
+  f32x16 s[QB];
+#pragma unroll
+  for (int qb = 0; qb < QB; qb++) s[qb] = f32x16{};
+#pragma unroll
+  for (int dk = 0; dk < C::DK; dk++) {
+#pragma unroll
+    for (int qb = 0; qb < QB; qb++)
+      s[qb] = __builtin_amdgcn_mfma_f32_32x32x16_bf16(kf[dk], qf[qb][dk], s[qb], 0, 0, 0);
+  }
+
+  // V^T fragments for O^T += V^T P^T, requested now so they arrive during the softmax.
+  bf16x8 vf[C::DB][2];
+#pragma unroll
+  for (int db = 0; db < C::DB; db++) {
+#pragma unroll
+    for (int ks = 0; ks < 2; ks++) {
+      const int r0 = 32 * sb + 16 * ks + vrow;
+      const int col = 32 * db + vcol;
+      const bf16x4 v0 = lds_read_tr16(Vt + tile_off<D>(r0, col));
+      const bf16x4 v1 = lds_read_tr16(Vt + tile_off<D>(r0 + 8, col));
+      vf[db][ks] = __builtin_shufflevector(v0, v1, 0, 1, 2, 3, 4, 5, 6, 7);
+    }
+  }
+
+  // Register i of s holds key kb0 + 8*(i/4) + 4*h + i%4 for query qw0 + 32*qb + c.
+  float t2[QB];
+  bool grow = false;
+#pragma unroll
+  for (int qb = 0; qb < QB; qb++) {
+    if (MASKED) {
+      // hide key kb0 + off_i when off_i > lim (a future key, or a key >= N)
+      int lim = N - 1 - kb0;
+      if (CAUSAL) lim = min(lim, qw0 + qb * 32 + c - kb0);
+      lim -= 4 * h;
+#pragma unroll
+      for (int i = 0; i < 16; i++)
+        if (8 * (i >> 2) + (i & 3) > lim) s[qb][i] = -INFINITY;
+    }
+    const float mx = half_swap_max(max16(s[qb]));
+    t2[qb] = MASKED && mx == -INFINITY ? -INFINITY : mx * scale_log2;
+    grow |= t2[qb] > st.m2[qb] + kRescaleSlack;
+  }
+  if (__any(grow)) {
+#pragma unroll
+    for (int qb = 0; qb < QB; qb++) {
+      const float mn = __builtin_fmaxf(st.m2[qb], t2[qb]);
+      const float ref = (mn == -INFINITY) ? 0.f : mn;
+      const float alpha = fast_exp2(st.m2[qb] - ref);  // 0 while nothing was seen yet
+      st.l[qb] *= alpha;
+#pragma unroll
+      for (int db = 0; db < C::DB; db++) st.acc[qb][db] *= alpha;
+      st.m2[qb] = mn;
+    }
+  }
+
+  // P = 2^(s*scale_log2 - m), row sum from fp32 P, bf16 P as the B operand of O^T.
+  bf16x8 pf[QB][2];
+#pragma unroll
+  for (int qb = 0; qb < QB; qb++) {
+    const float nref = (st.m2[qb] == -INFINITY) ? 0.f : -st.m2[qb];
+    float p[16];
+#pragma unroll
+    for (int i = 0; i < 16; i++) p[i] = fast_exp2(__builtin_fmaf(s[qb][i], scale_log2, nref));
+    st.l[qb] += sum16(p);
+#pragma unroll
+    for (int ks = 0; ks < 2; ks++)
+#pragma unroll
+      for (int e = 0; e < 8; e++) pf[qb][ks][e] = (bf16)p[8 * ks + e];
+  }
+
+  // O^T[d][query] += V^T[d][key] P^T[key][query], 16 keys per MFMA.
+#pragma unroll
+  for (int db = 0; db < C::DB; db++) {
+#pragma unroll
+    for (int ks = 0; ks < 2; ks++) {
+#pragma unroll
+      for (int qb = 0; qb < QB; qb++)
+        st.acc[qb][db] = __builtin_amdgcn_mfma_f32_32x32x16_bf16(vf[db][ks], pf[qb][ks],
+                                                                 st.acc[qb][db], 0, 0, 0);
+    }
+  }
+}
+
+#else
+template <int D, bool CAUSAL, bool MASKED, int QB, int NW, int BC>
+__device__ __forceinline__ void consume_sub(const char* __restrict__ Kt,
+                                            const char* __restrict__ Vt, int sb, int kb0, int qw0,
+                                            int N, float scale_log2, int c, int h, int vrow,
+                                            int vcol, const bf16x8 (&qf)[QB][D / 16],
+                                            RowState<QB, D / 32>& st) {
+  using C = Bf16Cfg<D, QB, NW, BC>;
+  // S^T[key][query] for 32 keys x 32 queries per qb.
+  f32x16 s[QB];
+#pragma unroll
+  for (int qb = 0; qb < QB; qb++) s[qb] = f32x16{};
+#pragma unroll
+  for (int dk = 0; dk < C::DK; dk++) {
+    const bf16x8 kf = lds_read_b128(Kt + tile_off<D>(32 * sb + c, 16 * dk + 8 * h));
+#pragma unroll
+    for (int qb = 0; qb < QB; qb++)
+      s[qb] = __builtin_amdgcn_mfma_f32_32x32x16_bf16(kf, qf[qb][dk], s[qb], 0, 0, 0);
+  }
+
+  // Register i of s holds key kb0 + 8*(i/4) + 4*h + i%4 for query qw0 + 32*qb + c.
+  float t2[QB];
+  bool grow = false;
+#pragma unroll
+  for (int qb = 0; qb < QB; qb++) {
+    if (MASKED) {
+      // hide key kb0 + off_i when off_i > lim (a future key, or a key >= N)
+      int lim = N - 1 - kb0;
+      if (CAUSAL) lim = min(lim, qw0 + qb * 32 + c - kb0);
+      lim -= 4 * h;
+#pragma unroll
+      for (int i = 0; i < 16; i++)
+        if (8 * (i >> 2) + (i & 3) > lim) s[qb][i] = -INFINITY;
+    }
+    const float mx = half_swap_max(max16(s[qb]));
+    t2[qb] = MASKED && mx == -INFINITY ? -INFINITY : mx * scale_log2;
+    grow |= t2[qb] > st.m2[qb] + kRescaleSlack;
+  }
+  if (__any(grow)) {
+#pragma unroll
+    for (int qb = 0; qb < QB; qb++) {
+      const float mn = __builtin_fmaxf(st.m2[qb], t2[qb]);
+      const float ref = (mn == -INFINITY) ? 0.f : mn;
+      const float alpha = fast_exp2(st.m2[qb] - ref);  // 0 while nothing was seen yet
+      st.l[qb] *= alpha;
+#pragma unroll
+      for (int db = 0; db < C::DB; db++) st.acc[qb][db] *= alpha;
+      st.m2[qb] = mn;
+    }
+  }
+
+  // P = 2^(s*scale_log2 - m), row sum from fp32 P, bf16 P as the B operand of O^T.
+  bf16x8 pf[QB][2];
+#pragma unroll
+  for (int qb = 0; qb < QB; qb++) {
+    const float nref = (st.m2[qb] == -INFINITY) ? 0.f : -st.m2[qb];
+    float p[16];
+#pragma unroll
+    for (int i = 0; i < 16; i++) p[i] = fast_exp2(__builtin_fmaf(s[qb][i], scale_log2, nref));
+    st.l[qb] += sum16(p);
+#pragma unroll
+    for (int ks = 0; ks < 2; ks++)
+#pragma unroll
+      for (int e = 0; e < 8; e++) pf[qb][ks][e] = (bf16)p[8 * ks + e];
+  }
+
+  // O^T[d][query] += V^T[d][key] P^T[key][query], 16 keys per MFMA.
+#pragma unroll
+  for (int db = 0; db < C::DB; db++) {
+#pragma unroll
+    for (int ks = 0; ks < 2; ks++) {
+      const int r0 = 32 * sb + 16 * ks + vrow;
+      const int col = 32 * db + vcol;
+      const bf16x4 v0 = lds_read_tr16(Vt + tile_off<D>(r0, col));
+      const bf16x4 v1 = lds_read_tr16(Vt + tile_off<D>(r0 + 8, col));
+      const bf16x8 vf = __builtin_shufflevector(v0, v1, 0, 1, 2, 3, 4, 5, 6, 7);
+#pragma unroll
+      for (int qb = 0; qb < QB; qb++)
+        st.acc[qb][db] =
+            __builtin_amdgcn_mfma_f32_32x32x16_bf16(vf, pf[qb][ks], st.acc[qb][db], 0, 0, 0);
+    }
+  }
+}
+
+#endif
+
+// Consume one [BC][D] K/V tile held in LDS, 32 keys at a time.
 template <int D, bool CAUSAL, int QB, int NW, int BC>
 __device__ __forceinline__ void consume_tile(const char* __restrict__ Kt,
                                              const char* __restrict__ Vt, int j, int qw0, int N,
@@ -99,95 +313,24 @@ __device__ __forceinline__ void consume_tile(const char* __restrict__ Kt,
   for (int sb = 0; sb < C::NSUB; sb++) {
     const int kb0 = j * BC + sb * 32;  // first key of this 32-key sub-block
     if (CAUSAL && kb0 > qw0 + C::R - 1) break;  // above the diagonal for every row of the wave
-    const bool masked = (kb0 + 31 >= N) || (CAUSAL && kb0 + 31 > qw0);
-
-    // S^T[key][query] for 32 keys x 32 queries per qb.
-    f32x16 s[QB];
-#pragma unroll
-    for (int qb = 0; qb < QB; qb++) s[qb] = f32x16{};
-#pragma unroll
-    for (int dk = 0; dk < C::DK; dk++) {
-      const bf16x8 kf = lds_read_b128(Kt + tile_off<D>(32 * sb + c, 16 * dk + 8 * h));
-#pragma unroll
-      for (int qb = 0; qb < QB; qb++)
-        s[qb] = __builtin_amdgcn_mfma_f32_32x32x16_bf16(kf, qf[qb][dk], s[qb], 0, 0, 0);
-    }
-
-    // Register i of s holds key kb0 + 8*(i/4) + 4*h + i%4 for query qw0 + 32*qb + c.
-    float t2[QB];
-    bool grow = false;
-#pragma unroll
-    for (int qb = 0; qb < QB; qb++) {
-      if (masked) {
-        const int qrow = qw0 + qb * 32 + c;
-#pragma unroll
-        for (int i = 0; i < 16; i++) {
-          const int key = kb0 + 8 * (i >> 2) + 4 * h + (i & 3);
-          if (key >= N || (CAUSAL && key > qrow)) s[qb][i] = -INFINITY;
-        }
-      }
-      float mx = s[qb][0];
-#pragma unroll
-      for (int i = 1; i < 16; i++) mx = fmaxf(mx, s[qb][i]);
-      mx = half_swap_max(mx);
-      t2[qb] = (mx == -INFINITY) ? -INFINITY : mx * scale_log2;
-      grow |= t2[qb] > st.m2[qb] + kRescaleSlack;
-    }
-    if (__any(grow)) {
-#pragma unroll
-      for (int qb = 0; qb < QB; qb++) {
-        const float mn = fmaxf(st.m2[qb], t2[qb]);
-        const float ref = (mn == -INFINITY) ? 0.f : mn;
-        const float alpha = fast_exp2(st.m2[qb] - ref);  // 0 while nothing was seen yet
-        st.l[qb] *= alpha;
-#pragma unroll
-        for (int db = 0; db < C::DB; db++) st.acc[qb][db] *= alpha;
-        st.m2[qb] = mn;
-      }
-    }
-
-    // P = 2^(s*scale_log2 - m), row sum from fp32 P, bf16 P as the B operand of O^T.
-    bf16x8 pf[QB][2];
-#pragma unroll
-    for (int qb = 0; qb < QB; qb++) {
-      const float ref = (st.m2[qb] == -INFINITY) ? 0.f : st.m2[qb];
-      float p[16];
-      float rs = 0.f;
-#pragma unroll
-      for (int i = 0; i < 16; i++) {
-        float e = fast_exp2(__builtin_fmaf(s[qb][i], scale_log2, -ref));
-        if (masked) e = (s[qb][i] == -INFINITY) ? 0.f : e;
-        p[i] = e;
-        rs += e;
-      }
-      st.l[qb] += rs;
-#pragma unroll
-      for (int ks = 0; ks < 2; ks++)
-#pragma unroll
-        for (int e = 0; e < 8; e++) pf[qb][ks][e] = (bf16)p[8 * ks + e];
-    }
-
-    // O^T[d][query] += V^T[d][key] P^T[key][query], 16 keys per MFMA.
-#pragma unroll
-    for (int db = 0; db < C::DB; db++) {
-#pragma unroll
-      for (int ks = 0; ks < 2; ks++) {
-        const int r0 = 32 * sb + 16 * ks + vrow;
-        const int col = 32 * db + vcol;
-        const bf16x4 v0 = lds_read_tr16(Vt + tile_off<D>(r0, col));
-        const bf16x4 v1 = lds_read_tr16(Vt + tile_off<D>(r0 + 8, col));
-        const bf16x8 vf = __builtin_shufflevector(v0, v1, 0, 1, 2, 3, 4, 5, 6, 7);
-#pragma unroll
-        for (int qb = 0; qb < QB; qb++)
-          st.acc[qb][db] =
-              __builtin_amdgcn_mfma_f32_32x32x16_bf16(vf, pf[qb][ks], st.acc[qb][db], 0, 0, 0);
-      }
+    if ((kb0 + 31 >= N) || (CAUSAL && kb0 + 31 > qw0)) {
+      consume_sub<D, CAUSAL, true, QB, NW, BC>(Kt, Vt, sb, kb0, qw0, N, scale_log2, c, h, vrow,
+                                               vcol, qf, st);
+    } else {
+      consume_sub<D, CAUSAL, false, QB, NW, BC>(Kt, Vt, sb, kb0, qw0, N, scale_log2, c, h, vrow,
+                                                vcol, qf, st);
     }
   }
 }
 
+// Minimum waves per SIMD the register allocation must allow (tuning knob; 1 = up to 512 VGPRs).
+#ifndef FA_MIN_WAVES_PER_EU
+#define FA_MIN_WAVES_PER_EU 1
+#endif
+
 template <int D, bool CAUSAL, int QB, int NW, int BC>
-__global__ __launch_bounds__(NW * 64) void fa_fwd_bf16_kernel(Bf16Args a) {
+__global__ __launch_bounds__(NW * 64) __attribute__((amdgpu_waves_per_eu(FA_MIN_WAVES_PER_EU)))
+void fa_fwd_bf16_kernel(Bf16Args a) {
   using C = Bf16Cfg<D, QB, NW, BC>;
   // Two stages, each with its own K and V array: separate objects let the compiler see that the
   // tile being read and the tile being filled never alias.

@@ -1,11 +1,13 @@
 // fp32 attention forward kernel: every step in fp32 on the vector ALUs (no bf16 anywhere).
 //
-// Same method as the bf16 kernel ("Understanding FlashAttention Pt 1", §2.4 and §3.1;
-// "FlashAttention-2 -- Deeper Math", Fixes 1-4 and causal tile skipping), laid out for
-// precision rather than speed: one thread owns one query row (its q, its running maximum, sum and
-// unnormalised output stay in registers), a workgroup owns 128 consecutive rows of one head, and
-// 32-key K/V tiles are staged through LDS and read as broadcasts. The reference maximum is the
-// exact running maximum (rescale whenever it moves).
+// Laid out for precision rather than speed. One thread owns one query row: its q, its running
+// maximum m, running sum l and unnormalised output a stay in registers, and the keys are folded in
+// one at a time with the scalar online recurrence ("Understanding FlashAttention Pt 1", §2.3:
+// m_j = max(m_{j-1}, x_j), l_j = l_{j-1} e^{m_{j-1} - m_j} + e^{x_j - m_j}, with a rescaled the
+// same way and o = a / l at the end). A workgroup owns 128 consecutive query rows of one head;
+// K/V tiles are staged through LDS and read as broadcasts; causal tiles above the workgroup's last
+// row are never loaded ("FlashAttention-2 -- Deeper Math", causal tile skipping). Scores are kept
+// in base 2 and the logsumexp is written in natural-log units.
 #pragma once
 
 #include "fa_device.h"
@@ -49,11 +51,9 @@ __global__ __launch_bounds__(kF32BlockQ) void fa_fwd_f32_kernel(F32Args a) {
   }
   float m2 = -INFINITY, l = 0.f;
 
-  const int n_kt_all = (N + kF32BlockK - 1) / kF32BlockK;
-  const int n_kt = CAUSAL ? min(n_kt_all, (min(q0 + kF32BlockQ, N) - 1) / kF32BlockK + 1)
-                          : n_kt_all;
-  for (int j = 0; j < n_kt; j++) {
-    const int k0 = j * kF32BlockK;
+  // keys this workgroup needs: all N, or (causal) up to its last row
+  const int n_keys = CAUSAL ? min(N, q0 + kF32BlockQ) : N;
+  for (int k0 = 0; k0 < n_keys; k0 += kF32BlockK) {
     __syncthreads();
     for (int e = threadIdx.x; e < kF32BlockK * D; e += kF32BlockQ) {
       const int r = e / D, t = e % D;
@@ -62,33 +62,26 @@ __global__ __launch_bounds__(kF32BlockQ) void fa_fwd_f32_kernel(F32Args a) {
       Vs[r][t] = in ? Vh[(size_t)(k0 + r) * D + t] : 0.f;
     }
     __syncthreads();
-
-    float s[kF32BlockK];
-    float mx = -INFINITY;
-#pragma unroll
-    for (int r = 0; r < kF32BlockK; r++) {
+    const int kend = min(kF32BlockK, n_keys - k0);
+#pragma unroll 1
+    for (int r = 0; r < kend; r++) {
+      if (CAUSAL && k0 + r > qrow) break;  // later keys of this tile are in the future too
       float dot = 0.f;
 #pragma unroll
       for (int t = 0; t < D; t++) dot = __builtin_fmaf(qr[t], Ks[r][t], dot);
-      const int key = k0 + r;
-      const bool vis = key < N && (!CAUSAL || key <= qrow);
-      s[r] = vis ? dot * a.scale_log2 : -INFINITY;
-      mx = fmaxf(mx, s[r]);
-    }
-    const float mn = fmaxf(m2, mx);
-    const float ref = (mn == -INFINITY) ? 0.f : mn;  // no visible key yet: any finite reference
-    const float alpha = exp2f(m2 - ref);
-    l *= alpha;
+      const float s2 = dot * a.scale_log2;
+      if (s2 > m2) {  // the maximum moves: rescale what was accumulated under the old one
+        const float alpha = exp2f(m2 - s2);  // 0 for the first key (m2 = -inf)
+        l *= alpha;
 #pragma unroll
-    for (int t = 0; t < D; t++) o[t] *= alpha;
-#pragma unroll
-    for (int r = 0; r < kF32BlockK; r++) {
-      const float p = (s[r] == -INFINITY) ? 0.f : exp2f(s[r] - ref);
+        for (int t = 0; t < D; t++) o[t] *= alpha;
+        m2 = s2;
+      }
+      const float p = exp2f(s2 - m2);
       l += p;
 #pragma unroll
       for (int t = 0; t < D; t++) o[t] = __builtin_fmaf(p, Vs[r][t], o[t]);
     }
-    m2 = mn;
   }
 
   if (qrow < N) {
