@@ -8,6 +8,7 @@
 
 #include "fa.h"
 #include "fa_fwd_bf16.h"
+#include "fa_fwd_bf16_pipe.h"
 #include "fa_fwd_f32.h"
 
 namespace {
@@ -59,12 +60,21 @@ int check_args(const void* q, const void* k, const void* v, const void* o, const
   return FA_OK;
 }
 
+#ifndef FA_PIPELINE
+#define FA_PIPELINE 1
+#endif
+
 template <int D, bool CAUSAL>
 hipError_t launch_bf16(fa::Bf16Args a, hipStream_t s) {
   void* args[] = {&a};
-  return hipLaunchKernel(
-      reinterpret_cast<const void*>(&fa::fa_fwd_bf16_kernel<D, CAUSAL, kQB, kNW, kBC>),
-      dim3(a.n_qblk * a.BH), dim3(kNW * 64), args, 0, s);
+#if FA_PIPELINE
+  static_assert(kQB == 1, "the pipelined kernel owns 32 rows per wave");
+  const void* k = reinterpret_cast<const void*>(&fa::fa_fwd_bf16_pipe_kernel<D, CAUSAL, kNW, kBC>);
+#else
+  const void* k =
+      reinterpret_cast<const void*>(&fa::fa_fwd_bf16_kernel<D, CAUSAL, kQB, kNW, kBC>);
+#endif
+  return hipLaunchKernel(k, dim3(a.n_qblk * a.BH), dim3(kNW * 64), args, 0, s);
 }
 
 template <int D, bool CAUSAL>

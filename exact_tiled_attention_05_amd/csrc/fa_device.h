@@ -62,6 +62,18 @@ __device__ inline void global_to_lds16(const void* g, char* lds) {
 }
 
 __device__ inline void wait_vmem_all() { asm volatile("s_waitcnt vmcnt(0)" ::: "memory"); }
+// Workgroup barrier without a memory fence. Used where each wave has already waited for its own
+// direct-to-LDS loads (vmcnt) and every LDS read of the buffer about to be refilled has been
+// consumed: the barrier then only has to order the waves.
+__device__ inline void barrier_only() { __builtin_amdgcn_s_barrier(); }
+
+// Wait until at most N vector-memory operations of this wave are outstanding (they complete in
+// issue order, so everything issued before the last N is done).
+template <int N>
+__device__ inline void wait_vmem_until() {
+  static_assert(N >= 0 && N < 64, "vmcnt range");
+  asm volatile("s_waitcnt vmcnt(%0)" ::"n"(N) : "memory");
+}
 
 // Value held by the lane 32 positions away (lane l <-> l ^ 32), combined with op.
 __device__ inline float half_swap_max(float x) {

@@ -43,6 +43,22 @@ constexpr float kRescaleSlack = 2.0f;
 #ifndef FA_HOIST_LDS
 #define FA_HOIST_LDS 0
 #endif
+// Tuning knob: raise the wave's issue priority while it issues a cluster of MFMAs, so that of two
+// waves sharing a SIMD the one feeding the matrix core is issued first and the other's softmax
+// instructions fill the gaps.
+#ifndef FA_SETPRIO
+#define FA_SETPRIO 1
+#endif
+__device__ __forceinline__ void mfma_prio_begin() {
+#if FA_SETPRIO
+  __builtin_amdgcn_s_setprio(1);
+#endif
+}
+__device__ __forceinline__ void mfma_prio_end() {
+#if FA_SETPRIO
+  __builtin_amdgcn_s_setprio(0);
+#endif
+}
 
 struct Bf16Args {
   const bf16* q;
@@ -135,12 +151,14 @@ __device__ __forceinline__ void consume_sub(const char* __restrict__ Kt,
   f32x16 s[QB];
 #pragma unroll
   for (int qb = 0; qb < QB; qb++) s[qb] = f32x16{};
+  mfma_prio_begin();
 #pragma unroll
   for (int dk = 0; dk < C::DK; dk++) {
 #pragma unroll
     for (int qb = 0; qb < QB; qb++)
       s[qb] = __builtin_amdgcn_mfma_f32_32x32x16_bf16(kf[dk], qf[qb][dk], s[qb], 0, 0, 0);
   }
+  mfma_prio_end();
 
   // V^T fragments for O^T += V^T P^T, requested now so they arrive during the softmax.
   bf16x8 vf[C::DB][2];
@@ -203,6 +221,7 @@ __device__ __forceinline__ void consume_sub(const char* __restrict__ Kt,
   }
 
   // O^T[d][query] += V^T[d][key] P^T[key][query], 16 keys per MFMA.
+  mfma_prio_begin();
 #pragma unroll
   for (int db = 0; db < C::DB; db++) {
 #pragma unroll
@@ -213,6 +232,7 @@ __device__ __forceinline__ void consume_sub(const char* __restrict__ Kt,
                                                                  st.acc[qb][db], 0, 0, 0);
     }
   }
+  mfma_prio_end();
 }
 
 #else
@@ -227,6 +247,7 @@ __device__ __forceinline__ void consume_sub(const char* __restrict__ Kt,
   f32x16 s[QB];
 #pragma unroll
   for (int qb = 0; qb < QB; qb++) s[qb] = f32x16{};
+  mfma_prio_begin();
 #pragma unroll
   for (int dk = 0; dk < C::DK; dk++) {
     const bf16x8 kf = lds_read_b128(Kt + tile_off<D>(32 * sb + c, 16 * dk + 8 * h));
@@ -234,6 +255,7 @@ __device__ __forceinline__ void consume_sub(const char* __restrict__ Kt,
     for (int qb = 0; qb < QB; qb++)
       s[qb] = __builtin_amdgcn_mfma_f32_32x32x16_bf16(kf, qf[qb][dk], s[qb], 0, 0, 0);
   }
+  mfma_prio_end();
 
   // Register i of s holds key kb0 + 8*(i/4) + 4*h + i%4 for query qw0 + 32*qb + c.
   float t2[QB];
@@ -282,6 +304,7 @@ __device__ __forceinline__ void consume_sub(const char* __restrict__ Kt,
   }
 
   // O^T[d][query] += V^T[d][key] P^T[key][query], 16 keys per MFMA.
+  mfma_prio_begin();
 #pragma unroll
   for (int db = 0; db < C::DB; db++) {
 #pragma unroll
@@ -297,6 +320,7 @@ __device__ __forceinline__ void consume_sub(const char* __restrict__ Kt,
             __builtin_amdgcn_mfma_f32_32x32x16_bf16(vf, pf[qb][ks], st.acc[qb][db], 0, 0, 0);
     }
   }
+  mfma_prio_end();
 }
 
 #endif
@@ -340,7 +364,8 @@ void fa_fwd_bf16_kernel(Bf16Args a) {
   __shared__ __attribute__((aligned(1024))) char sV1[C::TILE_BYTES];
 
   const int lane = threadIdx.x & 63;
-  const int wave = threadIdx.x >> 6;
+  // the wave index is the same for all 64 lanes: keep it (and everything derived from it) scalar
+  const int wave = __builtin_amdgcn_readfirstlane(threadIdx.x >> 6);
   const int c = lane & 31;  // query column (S^T, O^T) / key row (K operand)
   const int h = lane >> 5;  // lane half: selects the k-slot half of MFMA operands
   const int N = a.N;
