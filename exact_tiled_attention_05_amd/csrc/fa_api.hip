@@ -8,7 +8,6 @@
 
 #include "fa.h"
 #include "fa_fwd_bf16.h"
-#include "fa_fwd_bf16_pipe.h"
 #include "fa_fwd_f32.h"
 
 namespace {
@@ -16,21 +15,6 @@ namespace {
 constexpr int kVersion = 100;  // 0.1.0
 constexpr int kMaxN = 1 << 22;
 constexpr int kMaxBH = 65535;  // grid y of the fp32 kernel; also keeps bf16 grids < 2^31
-
-// Kernel shape for the bf16 path: rows per wave = 32*QB, waves per workgroup = NW, key tile BC.
-// (Overridable at build time for tuning sweeps.)
-#ifndef FA_QB
-#define FA_QB 1
-#endif
-#ifndef FA_NW
-#define FA_NW 8
-#endif
-#ifndef FA_BC
-#define FA_BC 64
-#endif
-constexpr int kQB = FA_QB;
-constexpr int kNW = FA_NW;
-constexpr int kBC = FA_BC;
 
 bool ranges_overlap(const void* a, size_t na, const void* b, size_t nb) {
   const uintptr_t x = reinterpret_cast<uintptr_t>(a), y = reinterpret_cast<uintptr_t>(b);
@@ -60,21 +44,11 @@ int check_args(const void* q, const void* k, const void* v, const void* o, const
   return FA_OK;
 }
 
-#ifndef FA_PIPELINE
-#define FA_PIPELINE 1
-#endif
-
 template <int D, bool CAUSAL>
 hipError_t launch_bf16(fa::Bf16Args a, hipStream_t s) {
   void* args[] = {&a};
-#if FA_PIPELINE
-  static_assert(kQB == 1, "the pipelined kernel owns 32 rows per wave");
-  const void* k = reinterpret_cast<const void*>(&fa::fa_fwd_bf16_pipe_kernel<D, CAUSAL, kNW, kBC>);
-#else
-  const void* k =
-      reinterpret_cast<const void*>(&fa::fa_fwd_bf16_kernel<D, CAUSAL, kQB, kNW, kBC>);
-#endif
-  return hipLaunchKernel(k, dim3(a.n_qblk * a.BH), dim3(kNW * 64), args, 0, s);
+  return hipLaunchKernel(reinterpret_cast<const void*>(&fa::fa_fwd_bf16_kernel<D, CAUSAL>),
+                         dim3(a.n_qblk * a.BH), dim3(fa::kNumWaves * 64), args, 0, s);
 }
 
 template <int D, bool CAUSAL>
@@ -105,15 +79,11 @@ int fa_fwd(const void* q, const void* k, const void* v, void* o, float* lse, int
   a.scale_log2 = scale > 0.f ? scale * fa::kLog2e : FLT_MIN;
   const hipStream_t s = static_cast<hipStream_t>(stream);
   hipError_t e;
-  if (d == 128) {
-    a.n_qblk = (N + fa::Bf16Cfg<128, kQB, kNW, kBC>::BLOCK_Q - 1) /
-               fa::Bf16Cfg<128, kQB, kNW, kBC>::BLOCK_Q;
+  a.n_qblk = (N + fa::kBlockQ - 1) / fa::kBlockQ;
+  if (d == 128)
     e = causal ? launch_bf16<128, true>(a, s) : launch_bf16<128, false>(a, s);
-  } else {
-    a.n_qblk = (N + fa::Bf16Cfg<64, kQB, kNW, kBC>::BLOCK_Q - 1) /
-               fa::Bf16Cfg<64, kQB, kNW, kBC>::BLOCK_Q;
+  else
     e = causal ? launch_bf16<64, true>(a, s) : launch_bf16<64, false>(a, s);
-  }
   return e == hipSuccess ? FA_OK : FA_ERR_LAUNCH;
 }
 

@@ -10,17 +10,16 @@
 // (s = scale * log2(e) * q.k in fp32) and LSE is converted to natural-log units on output.
 //
 // MI355X mapping.
-//   * Each wave owns 32*QB query rows (split-Q: no communication between waves, Fix 5). The wave
-//     computes S^T = K Q^T with v_mfma_f32_32x32x16_bf16, keys on the M axis and queries on the
-//     N axis, so every lane holds one query column and 16 of its keys per 32x32 block: the row
-//     maximum is an in-lane reduction plus one swap between the two 32-lane halves.
-//   * The S^T accumulator layout is directly the B operand of O^T += V^T P^T (same MFMA) after
-//     a permutation of the keys inside each 16-key step; V is read from its row-major LDS tile
-//     with transposing reads (ds_read_b64_tr_b16) in that same key order, so P never leaves
-//     registers and needs no cross-lane shuffle.
+//   * A workgroup is 8 waves and 256 query rows; each wave owns 32 rows (split-Q: no communication
+//     between waves, Fix 5). The wave computes S^T = K Q^T with v_mfma_f32_32x32x16_bf16, keys on
+//     the M axis and queries on the N axis, so every lane holds one query column and 16 of its
+//     keys per 32x32 block: the row maximum is an in-lane reduction plus one swap between the two
+//     32-lane halves.
+//   * The S^T accumulator layout is directly the B operand of O^T += V^T P^T (same MFMA) after a
+//     permutation of the keys inside each 16-key k-step: k-slot 8h + e of lane half h holds key
+//     8 (e / 4) + 4 h + e % 4. V is read from its row-major LDS tile with transposing reads
+//     (ds_read_b64_tr_b16) in that same key order, so P never leaves registers.
 //   * Q^T stays in registers for the whole kernel; O^T, m and l too.
-//   * K and V tiles go HBM -> LDS with direct 16-byte-per-lane loads (no VGPR staging), double
-//     buffered: tile j+1 is in flight while tile j is consumed; one barrier per tile.
 //   * Lazy rescaling: the reference maximum only moves when a new score exceeds it by more than
 //     kRescaleSlack (log2 units); otherwise p <= 2^kRescaleSlack and the alpha multiply of the
 //     accumulator is skipped for the whole wave. Any reference gives the same real-arithmetic
@@ -29,36 +28,39 @@
 //     >= 1/5 of their combined weight, so the bf16 rounding of its p cannot dominate a row's
 //     output; a large slack (2^8) lets a dominant late key carry a full 2^-9 relative rounding
 //     error into O.
-//   * Causal: tiles above the diagonal are never loaded or computed; sub-blocks below it run
-//     without a mask; only sub-blocks crossing the diagonal (or the ragged tail) are masked.
+//   * Causal: tiles above the diagonal are never loaded or computed; 32-key steps below it run
+//     without a mask; only steps crossing the diagonal (or the ragged tail) are masked.
+//
+// Instruction stream. Step g of a wave consumes 32 keys in two phases:
+//     V(g):   request the K fragments of step g+1 and the V^T fragments of step g from LDS, then
+//             the softmax of S(g) on the vector ALUs (mask, row maximum, reference update, rare
+//             rescale, exponentials, row sums, bf16 packing of P(g));
+//     M(g+1): one cluster of 16 MFMAs: S(g+1) = K(g+1) Q^T, then O^T += V^T(g) P^T(g).
+// A wave's vector instructions barely overlap its own MFMAs, but the other wave on the same SIMD
+// can keep the matrix core busy meanwhile. The 8 waves sit two per SIMD (waves w and w+4, as the
+// hardware places them) and form two groups, A = waves 0-3 and B = waves 4-7. The per-tile LDS
+// barrier sits at different points of the two groups' streams: group A meets it between M(g) and
+// V(g), group B between V(g-1) and M(g). When it releases, A starts a V phase while B starts an M
+// phase, so the two waves of every SIMD stay half a step apart (ping-pong) instead of being pulled
+// into the same phase at every tile.
+//
+// LDS protocol. Tiles are 64 keys (steps 2j and 2j+1 of tile j) in three stages, tile j in stage
+// j % 3. Crossing j writes the staged tile j+1 (held in registers) into stage (j+1) % 3, meets the
+// barrier, and starts the loads of tile j+2 into the staging registers. Group A crosses at the
+// start of step 2j+1, group B between V(2j) and M(2j+1). In both groups every read of tile j+1
+// (first: K of step 2j+2, requested in V(2j+1)) follows crossing j, and every read of tile j-2
+// (last: V^T of step 2j-3, requested in V(2j-3)) precedes crossing j-1, which precedes any write
+// of tile j+1. Every wave executes every crossing, also waves whose rows are all past N or whose
+// causal rows end early, so barrier counts always match.
 #pragma once
+
+#include <type_traits>
 
 #include "fa_device.h"
 
 namespace fa {
 
 constexpr float kRescaleSlack = 2.0f;
-
-// Tuning knob: request all K and V fragments of a 32-key sub-block ahead of their MFMAs.
-#ifndef FA_HOIST_LDS
-#define FA_HOIST_LDS 0
-#endif
-// Tuning knob: raise the wave's issue priority while it issues a cluster of MFMAs, so that of two
-// waves sharing a SIMD the one feeding the matrix core is issued first and the other's softmax
-// instructions fill the gaps.
-#ifndef FA_SETPRIO
-#define FA_SETPRIO 1
-#endif
-__device__ __forceinline__ void mfma_prio_begin() {
-#if FA_SETPRIO
-  __builtin_amdgcn_s_setprio(1);
-#endif
-}
-__device__ __forceinline__ void mfma_prio_end() {
-#if FA_SETPRIO
-  __builtin_amdgcn_s_setprio(0);
-#endif
-}
 
 struct Bf16Args {
   const bf16* q;
@@ -72,43 +74,73 @@ struct Bf16Args {
   float scale_log2;  // scale * log2(e)
 };
 
-template <int D, int QB, int NW, int BC>
-struct Bf16Cfg {
-  static constexpr int R = 32 * QB;           // query rows per wave
-  static constexpr int BLOCK_Q = R * NW;      // query rows per workgroup
-  static constexpr int TILE_BYTES = BC * D * 2;
-  static constexpr int NSUB = BC / 32;        // 32-key sub-blocks per tile
-  static constexpr int DK = D / 16;           // k-steps of Q K^T
-  static constexpr int DB = D / 32;           // 32-row blocks of O^T
-  static constexpr int LOADS = TILE_BYTES / 1024 / NW;  // 1 KB direct loads per wave per tile
-  static_assert(TILE_BYTES % (1024 * NW) == 0, "tile must split evenly over the waves");
-  static_assert(BC % 32 == 0, "key tile is a multiple of 32");
+constexpr int kNumWaves = 8;                    // waves per workgroup
+constexpr int kBlockQ = 32 * kNumWaves;         // query rows per workgroup
+constexpr int kBlockK = 64;                     // keys per LDS tile
+
+// LDS layouts: row-major tiles with padded rows, one padding per matrix so that each read pattern
+// is bank-conflict free and every address is a per-lane base plus a compile-time offset:
+//   K rows are 2*D + 16 bytes: the K operand reads one 16-byte chunk from 16 consecutive rows;
+//     a 16-byte row shift walks those 16 reads across all 64 banks.
+//   V rows are 2*D + 64 bytes: a transposing read touches 4 consecutive rows x 32 bytes per
+//     16-lane group (64 bytes per half-wave); a 64-byte row shift spreads the rows apart.
+template <int D>
+struct Layout {
+  static constexpr int KROW = 2 * D + 16;
+  static constexpr int VROW = 2 * D + 64;
+  static constexpr int K_BYTES = kBlockK * KROW;
+  static constexpr int V_BYTES = kBlockK * VROW;
 };
 
-// Issue the direct loads of one [BC][D] tile (rows key0..key0+BC-1, clamped to N-1) into `tile`.
-template <int D, int BC, int NW>
-__device__ inline void issue_tile(const bf16* __restrict__ src, int key0, int N, char* tile,
-                                  int wave, int lane) {
-  constexpr int CPR = D / 8;
-  constexpr int LOADS = BC * D * 2 / 1024 / NW;
+typedef unsigned u32x4 __attribute__((ext_vector_type(4)));
+
+// Register-staged tile copies. A [64][D] tile is split into 1 KB pieces of 64 16-byte chunks; wave
+// w copies pieces w, w+8, ...; lane L of piece i holds chunk 64*i + L of the row-major tile (row
+// (64*i + L) / (D/8), column chunk (64*i + L) % (D/8)).
+template <int D>
+struct TileRegs {
+  static constexpr int LOADS = kBlockK * D * 2 / 1024 / kNumWaves;
+  static_assert(kBlockK * D * 2 % (1024 * kNumWaves) == 0, "tile must split evenly over the waves");
+  u32x4 k[LOADS], v[LOADS];
+};
+
+// Loads go through raw buffer resources: piece i of wave w is the 1 KB at byte
+// key0 * 2D + (i * 8 + w) * 1024 of the head, lane L's 16 bytes at +16 L. The per-lane part of the
+// offset is the same for every piece and tile and the rest is scalar, so a load costs no vector
+// ALU work. Rows at or past N lie past the buffer's size and read as zeros (their scores are
+// masked).
+template <int D>
+__device__ __forceinline__ void load_tile(__amdgpu_buffer_rsrc_t rk, __amdgpu_buffer_rsrc_t rv,
+                                          int key0, int wave, int lane, TileRegs<D>& r) {
 #pragma unroll
-  for (int i = 0; i < LOADS; i++) {
-    const int blk = i * NW + wave;
-    const int slot = blk * 64 + lane;
-    const int row = slot / CPR;
-    const int pc = slot % CPR;
-    const int lc = pc ^ swz<D>(row);
-    const int grow = min(key0 + row, N - 1);
-    global_to_lds16(src + (size_t)grow * D + lc * 8, tile + blk * 1024);
+  for (int i = 0; i < TileRegs<D>::LOADS; i++) {
+    const int soff = key0 * (2 * D) + (i * kNumWaves + wave) * 1024;
+    r.k[i] = __builtin_bit_cast(u32x4, __builtin_amdgcn_raw_buffer_load_b128(rk, 16 * lane, soff, 0));
+    r.v[i] = __builtin_bit_cast(u32x4, __builtin_amdgcn_raw_buffer_load_b128(rv, 16 * lane, soff, 0));
   }
 }
 
-// Per-wave running state of the online softmax.
-template <int QB, int DB>
-struct RowState {
-  f32x16 acc[QB][DB];  // O^T accumulator: register i = d 8*(i/4) + 4*h + i%4 of block db
-  float m2[QB];        // reference maximum (log2 units), equal in both lane halves
-  float l[QB];         // this lane's part of the running sum (its 16 keys per 32-key block)
+template <int D>
+__device__ __forceinline__ void store_tile(char* __restrict__ Kt, char* __restrict__ Vt, int wave,
+                                           int lane, const TileRegs<D>& r) {
+  constexpr int CPR = D / 8;
+#pragma unroll
+  for (int i = 0; i < TileRegs<D>::LOADS; i++) {
+    const int slot = (i * kNumWaves + wave) * 64 + lane;
+    const int row = slot / CPR, chunk = slot % CPR;
+    *(FA_LDS u32x4*)(Kt + row * Layout<D>::KROW + 16 * chunk) = r.k[i];
+    *(FA_LDS u32x4*)(Vt + row * Layout<D>::VROW + 16 * chunk) = r.v[i];
+  }
+}
+
+// Fixed per-lane quantities of a wave, including the per-lane LDS bases:
+//   K operand (row 32*sb + c, column 16*dk + 8*h):  kbase + 32*dk + 32*KROW*sb
+//   V operand (rows 32*sb + 16*ks + vrow + 8*part, column 32*db + vcol):
+//                                                   vbase + 8*VROW*part + 64*db + (32*sb + 16*ks)*VROW
+struct Lane {
+  int c, h, qrow, qw0, N, last;
+  int kbase, vbase;
+  float sl2;
 };
 
 // Tree reductions over the 16 values a lane holds for one 32x32 block (short dependency chains).
@@ -130,337 +162,251 @@ __device__ __forceinline__ float sum16(const float (&p)[16]) {
   return (t[0] + t[1]) + (t[2] + t[3]);
 }
 
-// One 32-key sub-block: S^T = K Q^T, online softmax update, O^T += V^T P^T.
-// MASKED sub-blocks cross the causal diagonal or the ragged tail; their hidden scores become -inf
-// before the maximum, and exp2(-inf) = 0 removes them from the sums (scale_log2 is never 0 here:
-// the host runs scale 0 as the smallest normal float, which gives the same probabilities).
-#if FA_HOIST_LDS
-template <int D, bool CAUSAL, bool MASKED, int QB, int NW, int BC>
-__device__ __forceinline__ void consume_sub(const char* __restrict__ Kt,
-                                            const char* __restrict__ Vt, int sb, int kb0, int qw0,
-                                            int N, float scale_log2, int c, int h, int vrow,
-                                            int vcol, const bf16x8 (&qf)[QB][D / 16],
-                                            RowState<QB, D / 32>& st) {
-  using C = Bf16Cfg<D, QB, NW, BC>;
-  // S^T[key][query] for 32 keys x 32 queries per qb. All K fragments are requested before the
-  // first MFMA so that LDS latency overlaps the MFMA chain.
-  bf16x8 kf[C::DK];
+// K operand of one 32-key step (sub-block sb of the tile at Kt).
+template <int D>
+__device__ __forceinline__ void read_k(const char* __restrict__ Kt, int sb, const Lane& L,
+                                       bf16x8 (&kf)[D / 16]) {
+  constexpr int KROW = Layout<D>::KROW;
 #pragma unroll
-  for (int dk = 0; dk < C::DK; dk++)
-    kf[dk] = lds_read_b128(Kt + tile_off<D>(32 * sb + c, 16 * dk + 8 * h));
-  f32x16 s[QB];
-#pragma unroll
-  for (int qb = 0; qb < QB; qb++) s[qb] = f32x16{};
-  mfma_prio_begin();
-#pragma unroll
-  for (int dk = 0; dk < C::DK; dk++) {
-#pragma unroll
-    for (int qb = 0; qb < QB; qb++)
-      s[qb] = __builtin_amdgcn_mfma_f32_32x32x16_bf16(kf[dk], qf[qb][dk], s[qb], 0, 0, 0);
-  }
-  mfma_prio_end();
+  for (int dk = 0; dk < D / 16; dk++) kf[dk] = lds_read_b128(Kt + L.kbase + 32 * dk + 32 * KROW * sb);
+}
 
-  // V^T fragments for O^T += V^T P^T, requested now so they arrive during the softmax.
-  bf16x8 vf[C::DB][2];
+// V^T operand of one 32-key step, in the key order of the S^T accumulator.
+template <int D>
+__device__ __forceinline__ void read_v(const char* __restrict__ Vt, int sb, const Lane& L,
+                                       bf16x8 (&vf)[D / 32][2]) {
+  constexpr int VROW = Layout<D>::VROW;
 #pragma unroll
-  for (int db = 0; db < C::DB; db++) {
+  for (int db = 0; db < D / 32; db++)
 #pragma unroll
     for (int ks = 0; ks < 2; ks++) {
-      const int r0 = 32 * sb + 16 * ks + vrow;
-      const int col = 32 * db + vcol;
-      const bf16x4 v0 = lds_read_tr16(Vt + tile_off<D>(r0, col));
-      const bf16x4 v1 = lds_read_tr16(Vt + tile_off<D>(r0 + 8, col));
+      const char* p = Vt + L.vbase + 64 * db + (32 * sb + 16 * ks) * VROW;
+      const bf16x4 v0 = lds_read_tr16(p);
+      const bf16x4 v1 = lds_read_tr16(p + 8 * VROW);
       vf[db][ks] = __builtin_shufflevector(v0, v1, 0, 1, 2, 3, 4, 5, 6, 7);
     }
-  }
-
-  // Register i of s holds key kb0 + 8*(i/4) + 4*h + i%4 for query qw0 + 32*qb + c.
-  float t2[QB];
-  bool grow = false;
-#pragma unroll
-  for (int qb = 0; qb < QB; qb++) {
-    if (MASKED) {
-      // hide key kb0 + off_i when off_i > lim (a future key, or a key >= N)
-      int lim = N - 1 - kb0;
-      if (CAUSAL) lim = min(lim, qw0 + qb * 32 + c - kb0);
-      lim -= 4 * h;
-#pragma unroll
-      for (int i = 0; i < 16; i++)
-        if (8 * (i >> 2) + (i & 3) > lim) s[qb][i] = -INFINITY;
-    }
-    const float mx = half_swap_max(max16(s[qb]));
-    t2[qb] = MASKED && mx == -INFINITY ? -INFINITY : mx * scale_log2;
-    grow |= t2[qb] > st.m2[qb] + kRescaleSlack;
-  }
-  if (__any(grow)) {
-#pragma unroll
-    for (int qb = 0; qb < QB; qb++) {
-      const float mn = __builtin_fmaxf(st.m2[qb], t2[qb]);
-      const float ref = (mn == -INFINITY) ? 0.f : mn;
-      const float alpha = fast_exp2(st.m2[qb] - ref);  // 0 while nothing was seen yet
-      st.l[qb] *= alpha;
-#pragma unroll
-      for (int db = 0; db < C::DB; db++) st.acc[qb][db] *= alpha;
-      st.m2[qb] = mn;
-    }
-  }
-
-  // P = 2^(s*scale_log2 - m), row sum from fp32 P, bf16 P as the B operand of O^T.
-  bf16x8 pf[QB][2];
-#pragma unroll
-  for (int qb = 0; qb < QB; qb++) {
-    const float nref = (st.m2[qb] == -INFINITY) ? 0.f : -st.m2[qb];
-    float p[16];
-#pragma unroll
-    for (int i = 0; i < 16; i++) p[i] = fast_exp2(__builtin_fmaf(s[qb][i], scale_log2, nref));
-    st.l[qb] += sum16(p);
-#pragma unroll
-    for (int ks = 0; ks < 2; ks++)
-#pragma unroll
-      for (int e = 0; e < 8; e++) pf[qb][ks][e] = (bf16)p[8 * ks + e];
-  }
-
-  // O^T[d][query] += V^T[d][key] P^T[key][query], 16 keys per MFMA.
-  mfma_prio_begin();
-#pragma unroll
-  for (int db = 0; db < C::DB; db++) {
-#pragma unroll
-    for (int ks = 0; ks < 2; ks++) {
-#pragma unroll
-      for (int qb = 0; qb < QB; qb++)
-        st.acc[qb][db] = __builtin_amdgcn_mfma_f32_32x32x16_bf16(vf[db][ks], pf[qb][ks],
-                                                                 st.acc[qb][db], 0, 0, 0);
-    }
-  }
-  mfma_prio_end();
 }
 
-#else
-template <int D, bool CAUSAL, bool MASKED, int QB, int NW, int BC>
-__device__ __forceinline__ void consume_sub(const char* __restrict__ Kt,
-                                            const char* __restrict__ Vt, int sb, int kb0, int qw0,
-                                            int N, float scale_log2, int c, int h, int vrow,
-                                            int vcol, const bf16x8 (&qf)[QB][D / 16],
-                                            RowState<QB, D / 32>& st) {
-  using C = Bf16Cfg<D, QB, NW, BC>;
-  // S^T[key][query] for 32 keys x 32 queries per qb.
-  f32x16 s[QB];
-#pragma unroll
-  for (int qb = 0; qb < QB; qb++) s[qb] = f32x16{};
-  mfma_prio_begin();
-#pragma unroll
-  for (int dk = 0; dk < C::DK; dk++) {
-    const bf16x8 kf = lds_read_b128(Kt + tile_off<D>(32 * sb + c, 16 * dk + 8 * h));
-#pragma unroll
-    for (int qb = 0; qb < QB; qb++)
-      s[qb] = __builtin_amdgcn_mfma_f32_32x32x16_bf16(kf, qf[qb][dk], s[qb], 0, 0, 0);
-  }
-  mfma_prio_end();
+// Per-wave state.
+template <int D>
+struct WaveState {
+  bf16x8 qf[D / 16];     // Q^T operand (this wave's 32 rows)
+  f32x16 acc[D / 32];    // O^T accumulator: register i = d 8*(i/4) + 4*h + i%4 of block db
+  f32x16 s;              // S^T of the step whose softmax comes next
+  bf16x8 pf[2];          // P^T operand of the step whose PV product comes next
+  bf16x8 kf[D / 16];     // K operand of the next QK product
+  bf16x8 vf[D / 32][2];  // V^T operand of the next PV product
+  float m2, l;           // reference maximum (log2 units) and this lane's part of the row sum
+};
 
-  // Register i of s holds key kb0 + 8*(i/4) + 4*h + i%4 for query qw0 + 32*qb + c.
-  float t2[QB];
-  bool grow = false;
+// V phase, softmax part: P(g) from S(g). Hidden scores (keys past N, and with a causal mask keys
+// past the lane's row) become -inf before the maximum, and exp2(-inf) = 0 removes them from the
+// sums.
+template <int D, bool CAUSAL>
+__device__ __forceinline__ void softmax_step(int g, const Lane& L, WaveState<D>& st) {
+  constexpr int DB = D / 32;
+  f32x16& s = st.s;
+  const int kb0 = g * 32;
+  if ((kb0 + 31 >= L.N) || (CAUSAL && kb0 + 31 > L.qw0)) {
+    int lim = L.N - 1 - kb0;
+    if (CAUSAL) lim = min(lim, L.qrow - kb0);
+    lim -= 4 * L.h;
 #pragma unroll
-  for (int qb = 0; qb < QB; qb++) {
-    if (MASKED) {
-      // hide key kb0 + off_i when off_i > lim (a future key, or a key >= N)
-      int lim = N - 1 - kb0;
-      if (CAUSAL) lim = min(lim, qw0 + qb * 32 + c - kb0);
-      lim -= 4 * h;
-#pragma unroll
-      for (int i = 0; i < 16; i++)
-        if (8 * (i >> 2) + (i & 3) > lim) s[qb][i] = -INFINITY;
-    }
-    const float mx = half_swap_max(max16(s[qb]));
-    t2[qb] = MASKED && mx == -INFINITY ? -INFINITY : mx * scale_log2;
-    grow |= t2[qb] > st.m2[qb] + kRescaleSlack;
+    for (int i = 0; i < 16; i++)
+      if (8 * (i >> 2) + (i & 3) > lim) s[i] = -INFINITY;
   }
-  if (__any(grow)) {
+  // Every row of an active step sees at least one key (key 0 at step 0, its own diagonal key in
+  // the diagonal step, key kb0 < N in the tail step), so the maximum is finite; scale_log2 > 0
+  // (scale 0 runs as FLT_MIN), so t2 and, from the first step on, m2 are finite.
+  const float t2 = half_swap_max(max16(s)) * L.sl2;
+  if (__any(t2 > st.m2 + kRescaleSlack)) {
+    const float mn = __builtin_fmaxf(st.m2, t2);
+    const float alpha = fast_exp2(st.m2 - mn);  // 0 at the first step (m2 = -inf)
+    st.l *= alpha;
 #pragma unroll
-    for (int qb = 0; qb < QB; qb++) {
-      const float mn = __builtin_fmaxf(st.m2[qb], t2[qb]);
-      const float ref = (mn == -INFINITY) ? 0.f : mn;
-      const float alpha = fast_exp2(st.m2[qb] - ref);  // 0 while nothing was seen yet
-      st.l[qb] *= alpha;
-#pragma unroll
-      for (int db = 0; db < C::DB; db++) st.acc[qb][db] *= alpha;
-      st.m2[qb] = mn;
-    }
+    for (int db = 0; db < DB; db++) st.acc[db] *= alpha;
+    st.m2 = mn;
   }
-
-  // P = 2^(s*scale_log2 - m), row sum from fp32 P, bf16 P as the B operand of O^T.
-  bf16x8 pf[QB][2];
+  const float nref = -st.m2;
+  float p[16];
 #pragma unroll
-  for (int qb = 0; qb < QB; qb++) {
-    const float nref = (st.m2[qb] == -INFINITY) ? 0.f : -st.m2[qb];
-    float p[16];
+  for (int i = 0; i < 16; i++) p[i] = fast_exp2(__builtin_fmaf(s[i], L.sl2, nref));
 #pragma unroll
-    for (int i = 0; i < 16; i++) p[i] = fast_exp2(__builtin_fmaf(s[qb][i], scale_log2, nref));
-    st.l[qb] += sum16(p);
+  for (int ks = 0; ks < 2; ks++)
 #pragma unroll
-    for (int ks = 0; ks < 2; ks++)
-#pragma unroll
-      for (int e = 0; e < 8; e++) pf[qb][ks][e] = (bf16)p[8 * ks + e];
-  }
-
-  // O^T[d][query] += V^T[d][key] P^T[key][query], 16 keys per MFMA.
-  mfma_prio_begin();
-#pragma unroll
-  for (int db = 0; db < C::DB; db++) {
-#pragma unroll
-    for (int ks = 0; ks < 2; ks++) {
-      const int r0 = 32 * sb + 16 * ks + vrow;
-      const int col = 32 * db + vcol;
-      const bf16x4 v0 = lds_read_tr16(Vt + tile_off<D>(r0, col));
-      const bf16x4 v1 = lds_read_tr16(Vt + tile_off<D>(r0 + 8, col));
-      const bf16x8 vf = __builtin_shufflevector(v0, v1, 0, 1, 2, 3, 4, 5, 6, 7);
-#pragma unroll
-      for (int qb = 0; qb < QB; qb++)
-        st.acc[qb][db] =
-            __builtin_amdgcn_mfma_f32_32x32x16_bf16(vf, pf[qb][ks], st.acc[qb][db], 0, 0, 0);
-    }
-  }
-  mfma_prio_end();
+    for (int e = 0; e < 8; e++) st.pf[ks][e] = (bf16)p[8 * ks + e];
+  st.l += sum16(p);
+  // The packed P and the row sum exist here, before any barrier that follows in program order
+  // (pure arithmetic would otherwise be free to sink to its first use in the M phase).
+  asm volatile("" ::"v"(st.pf[0]), "v"(st.pf[1]), "v"(st.l));
 }
 
-#endif
-
-// Consume one [BC][D] K/V tile held in LDS, 32 keys at a time.
-template <int D, bool CAUSAL, int QB, int NW, int BC>
-__device__ __forceinline__ void consume_tile(const char* __restrict__ Kt,
-                                             const char* __restrict__ Vt, int j, int qw0, int N,
-                                             float scale_log2, int c, int h, int vrow, int vcol,
-                                             const bf16x8 (&qf)[QB][D / 16],
-                                             RowState<QB, D / 32>& st) {
-  using C = Bf16Cfg<D, QB, NW, BC>;
+// M phase: S(g+1) (when the wave has a step g+1), then O^T += V^T(g) P^T(g).
+template <int D>
+__device__ __forceinline__ void mfma_step(bool qk, WaveState<D>& st) {
+  constexpr int DK = D / 16, DB = D / 32;
+  if (qk) {
+    st.s = f32x16{};
 #pragma unroll
-  for (int sb = 0; sb < C::NSUB; sb++) {
-    const int kb0 = j * BC + sb * 32;  // first key of this 32-key sub-block
-    if (CAUSAL && kb0 > qw0 + C::R - 1) break;  // above the diagonal for every row of the wave
-    if ((kb0 + 31 >= N) || (CAUSAL && kb0 + 31 > qw0)) {
-      consume_sub<D, CAUSAL, true, QB, NW, BC>(Kt, Vt, sb, kb0, qw0, N, scale_log2, c, h, vrow,
-                                               vcol, qf, st);
-    } else {
-      consume_sub<D, CAUSAL, false, QB, NW, BC>(Kt, Vt, sb, kb0, qw0, N, scale_log2, c, h, vrow,
-                                                vcol, qf, st);
-    }
+    for (int dk = 0; dk < DK; dk++)
+      st.s = __builtin_amdgcn_mfma_f32_32x32x16_bf16(st.kf[dk], st.qf[dk], st.s, 0, 0, 0);
   }
+#pragma unroll
+  for (int ks = 0; ks < 2; ks++)
+#pragma unroll
+    for (int db = 0; db < DB; db++)
+      st.acc[db] = __builtin_amdgcn_mfma_f32_32x32x16_bf16(st.vf[db][ks], st.pf[ks], st.acc[db], 0, 0, 0);
 }
 
-// Minimum waves per SIMD the register allocation must allow (tuning knob; 1 = up to 512 VGPRs).
-#ifndef FA_MIN_WAVES_PER_EU
-#define FA_MIN_WAVES_PER_EU 1
-#endif
-
-template <int D, bool CAUSAL, int QB, int NW, int BC>
-__global__ __launch_bounds__(NW * 64) __attribute__((amdgpu_waves_per_eu(FA_MIN_WAVES_PER_EU)))
-void fa_fwd_bf16_kernel(Bf16Args a) {
-  using C = Bf16Cfg<D, QB, NW, BC>;
-  // Two stages, each with its own K and V array: separate objects let the compiler see that the
-  // tile being read and the tile being filled never alias.
-  __shared__ __attribute__((aligned(1024))) char sK0[C::TILE_BYTES];
-  __shared__ __attribute__((aligned(1024))) char sV0[C::TILE_BYTES];
-  __shared__ __attribute__((aligned(1024))) char sK1[C::TILE_BYTES];
-  __shared__ __attribute__((aligned(1024))) char sV1[C::TILE_BYTES];
+template <int D, bool CAUSAL>
+__global__ __launch_bounds__(kNumWaves * 64) void fa_fwd_bf16_kernel(Bf16Args a) {
+  constexpr int DK = D / 16;
+  constexpr int DB = D / 32;
+  __shared__ __attribute__((aligned(1024))) char sK0[Layout<D>::K_BYTES];
+  __shared__ __attribute__((aligned(1024))) char sK1[Layout<D>::K_BYTES];
+  __shared__ __attribute__((aligned(1024))) char sK2[Layout<D>::K_BYTES];
+  __shared__ __attribute__((aligned(1024))) char sV0[Layout<D>::V_BYTES];
+  __shared__ __attribute__((aligned(1024))) char sV1[Layout<D>::V_BYTES];
+  __shared__ __attribute__((aligned(1024))) char sV2[Layout<D>::V_BYTES];
 
   const int lane = threadIdx.x & 63;
   // the wave index is the same for all 64 lanes: keep it (and everything derived from it) scalar
   const int wave = __builtin_amdgcn_readfirstlane(threadIdx.x >> 6);
-  const int c = lane & 31;  // query column (S^T, O^T) / key row (K operand)
-  const int h = lane >> 5;  // lane half: selects the k-slot half of MFMA operands
+  const bool group_a = wave < kNumWaves / 2;  // waves w and w + 4 share a SIMD
   const int N = a.N;
 
   int bh, qblk;
   map_block<CAUSAL>(blockIdx.x, gridDim.x, a.BH, a.n_qblk, bh, qblk);
   const size_t head = (size_t)bh * N * D;
   const bf16* __restrict__ Qh = a.q + head;
-  const bf16* __restrict__ Kh = a.k + head;
-  const bf16* __restrict__ Vh = a.v + head;
-  const int q0 = qblk * C::BLOCK_Q;
-  const int qw0 = q0 + wave * C::R;  // first query row of this wave
+  // N * D * 2 <= 2^30 for N <= 2^22 and D <= 128
+  const __amdgpu_buffer_rsrc_t rk =
+      __builtin_amdgcn_make_buffer_rsrc((void*)(a.k + head), 0, N * D * 2, 0x00020000);
+  const __amdgpu_buffer_rsrc_t rv =
+      __builtin_amdgcn_make_buffer_rsrc((void*)(a.v + head), 0, N * D * 2, 0x00020000);
+  const int q0 = qblk * kBlockQ;
 
-  // Key tiles this workgroup visits (causal: none above its last query row).
-  const int n_kt_all = (N + BC - 1) / BC;
-  int n_kt = n_kt_all;
-  if (CAUSAL) n_kt = min(n_kt_all, (min(q0 + C::BLOCK_Q, N) - 1) / BC + 1);
+  Lane L;
+  L.c = lane & 31;
+  L.h = lane >> 5;
+  L.N = N;
+  L.sl2 = a.scale_log2;
+  L.qw0 = q0 + wave * 32;  // the wave's first query row
+  L.qrow = L.qw0 + L.c;    // this lane's query row
+  {
+    // V operand, transposing read: in 16-lane group g = lane/16, lane Lg = lane%16 addresses row
+    // vrow = 4*h + Lg/4 (+8 for the second half of the k-slots), column 16*(g&1) + 4*(Lg%4).
+    const int Lg = lane & 15;
+    const int vrow = 4 * L.h + (Lg >> 2);
+    const int vcol = 16 * ((lane >> 4) & 1) + 4 * (Lg & 3);
+    L.kbase = L.c * Layout<D>::KROW + 16 * L.h;
+    L.vbase = vrow * Layout<D>::VROW + 2 * vcol;
+  }
 
-  // Start streaming tile 0 before touching Q.
-  issue_tile<D, BC, NW>(Kh, 0, N, sK0, wave, lane);
-  issue_tile<D, BC, NW>(Vh, 0, N, sV0, wave, lane);
+  // Tiles of the workgroup (causal: up to its last row) and 32-key steps of this wave (causal: up
+  // to its own diagonal).
+  const int n_kt_all = (N + kBlockK - 1) / kBlockK;
+  const int n_kt = CAUSAL ? min(n_kt_all, (min(q0 + kBlockQ, N) - 1) / kBlockK + 1) : n_kt_all;
+  const int n_steps = 2 * n_kt;
+  // last step with a key this wave can see (-1: every row of the wave is past N)
+  L.last = L.qw0 >= N ? -1
+           : CAUSAL   ? min(n_steps - 1, (min(L.qw0 + 31, N - 1)) / 32)
+                      : (N - 1) / 32;
 
-  // Q^T as the B operand: lane (h, c) holds Q[row c][16*dk + 8*h .. +7] for each k-step dk.
-  bf16x8 qf[QB][C::DK];
+  // Prologue: tile 0 into stage 0, Q into registers, tile 1 into the staging registers, S(0).
+  TileRegs<D> stage;
+  load_tile<D>(rk, rv, 0, wave, lane, stage);
+  WaveState<D> st;
 #pragma unroll
-  for (int qb = 0; qb < QB; qb++) {
-    const int row = qw0 + qb * 32 + c;
+  for (int dk = 0; dk < DK; dk++)
+    st.qf[dk] = (L.qrow < N)
+                    ? *reinterpret_cast<const bf16x8*>(Qh + (size_t)L.qrow * D + dk * 16 + L.h * 8)
+                    : bf16x8{};
 #pragma unroll
-    for (int dk = 0; dk < C::DK; dk++) {
-      if (row < N) {
-        qf[qb][dk] = *reinterpret_cast<const bf16x8*>(Qh + (size_t)row * D + dk * 16 + h * 8);
-      } else {
-        qf[qb][dk] = bf16x8{};
+  for (int db = 0; db < DB; db++) st.acc[db] = f32x16{};
+  st.m2 = -INFINITY;
+  st.l = 0.f;
+  store_tile<D>(sK0, sV0, wave, lane, stage);
+  if (n_kt > 1) load_tile<D>(rk, rv, kBlockK, wave, lane, stage);
+  __syncthreads();
+  st.s = f32x16{};
+  if (L.last >= 0) {
+    read_k<D>(sK0, 0, L, st.kf);
+#pragma unroll
+    for (int dk = 0; dk < DK; dk++)
+      st.s = __builtin_amdgcn_mfma_f32_32x32x16_bf16(st.kf[dk], st.qf[dk], st.s, 0, 0, 0);
+  }
+
+  // Crossing j: staged tile j+1 into its stage, barrier, loads of tile j+2.
+  auto crossing = [&](char* __restrict__ Kn, char* __restrict__ Vn, int j) {
+    store_tile<D>(Kn, Vn, wave, lane, stage);
+    __syncthreads();
+    if (j + 2 < n_kt) load_tile<D>(rk, rv, (j + 2) * kBlockK, wave, lane, stage);
+  };
+
+  // Tile j in stage S (a compile-time constant, so every LDS address is a base plus an immediate
+  // and the compiler sees which array each access touches).
+  auto tile = [&](auto stage_c, int j) {
+    constexpr int S = decltype(stage_c)::value;
+    constexpr int SN = (S + 1) % 3;
+    const char* Kt = S == 0 ? sK0 : S == 1 ? sK1 : sK2;
+    const char* Vt = S == 0 ? sV0 : S == 1 ? sV1 : sV2;
+    char* Knext = SN == 0 ? sK0 : SN == 1 ? sK1 : sK2;
+    char* Vnext = SN == 0 ? sV0 : SN == 1 ? sV1 : sV2;
+    const bool has_next_tile = j + 1 < n_kt;
+    {  // step 2j
+      const int g = 2 * j;
+      if (g <= L.last) {
+        if (g + 1 <= L.last) read_k<D>(Kt, 1, L, st.kf);
+        read_v<D>(Vt, 0, L, st.vf);
+        softmax_step<D, CAUSAL>(g, L, st);
       }
+      __builtin_amdgcn_sched_barrier(0);
+      if (!group_a && has_next_tile) crossing(Knext, Vnext, j);
+      __builtin_amdgcn_sched_barrier(0);
+      if (g <= L.last) mfma_step<D>(g + 1 <= L.last, st);
+      __builtin_amdgcn_sched_barrier(0);
     }
-  }
-
-  RowState<QB, C::DB> st;
-#pragma unroll
-  for (int qb = 0; qb < QB; qb++) {
-    st.m2[qb] = -INFINITY;
-    st.l[qb] = 0.f;
-#pragma unroll
-    for (int db = 0; db < C::DB; db++) st.acc[qb][db] = f32x16{};
-  }
-
-  // V operand (A of O^T, transposing read): within the 16-lane group g = lane/16, lane L = lane%16
-  // addresses row 32*sb + 16*ks + 8*part + 4*h + L/4, column 32*db + 16*(g&1) + 4*(L%4).
-  const int Lg = lane & 15;
-  const int vrow = 4 * h + (Lg >> 2);
-  const int vcol = 16 * ((lane >> 4) & 1) + 4 * (Lg & 3);
-
-  // Tile j lives in stage j%2. At the top of each step: my loads of tile j are done, then the
-  // barrier makes everyone's loads visible and guarantees everyone has finished tile j-1, whose
-  // stage is refilled with tile j+1 while tile j is consumed.
-  for (int j = 0; j < n_kt; j += 2) {
-    wait_vmem_all();
-    __syncthreads();
-    if (j + 1 < n_kt) {
-      issue_tile<D, BC, NW>(Kh, (j + 1) * BC, N, sK1, wave, lane);
-      issue_tile<D, BC, NW>(Vh, (j + 1) * BC, N, sV1, wave, lane);
+    {  // step 2j+1
+      const int g = 2 * j + 1;
+      if (group_a && has_next_tile) crossing(Knext, Vnext, j);
+      __builtin_amdgcn_sched_barrier(0);
+      if (g <= L.last) {
+        if (g + 1 <= L.last) read_k<D>(Knext, 0, L, st.kf);
+        read_v<D>(Vt, 1, L, st.vf);
+        softmax_step<D, CAUSAL>(g, L, st);
+      }
+      __builtin_amdgcn_sched_barrier(0);
+      if (g <= L.last) mfma_step<D>(g + 1 <= L.last, st);
+      __builtin_amdgcn_sched_barrier(0);
     }
-    consume_tile<D, CAUSAL, QB, NW, BC>(sK0, sV0, j, qw0, N, a.scale_log2, c, h, vrow, vcol, qf,
-                                        st);
+  };
+  using I0 = std::integral_constant<int, 0>;
+  using I1 = std::integral_constant<int, 1>;
+  using I2 = std::integral_constant<int, 2>;
+  for (int j = 0; j < n_kt; j += 3) {
+    tile(I0{}, j);
     if (j + 1 >= n_kt) break;
-    wait_vmem_all();
-    __syncthreads();
-    if (j + 2 < n_kt) {
-      issue_tile<D, BC, NW>(Kh, (j + 2) * BC, N, sK0, wave, lane);
-      issue_tile<D, BC, NW>(Vh, (j + 2) * BC, N, sV0, wave, lane);
-    }
-    consume_tile<D, CAUSAL, QB, NW, BC>(sK1, sV1, j + 1, qw0, N, a.scale_log2, c, h, vrow, vcol,
-                                        qf, st);
+    tile(I1{}, j + 1);
+    if (j + 2 >= n_kt) break;
+    tile(I2{}, j + 2);
   }
 
   // Epilogue: O = a / l, LSE = ln2 * (m + log2 l).
+  const float lt = half_swap_sum(st.l);
+  if (L.qrow < N) {
+    const float inv = 1.0f / lt;
+    bf16* orow = a.o + head + (size_t)L.qrow * D;
 #pragma unroll
-  for (int qb = 0; qb < QB; qb++) {
-    const float lt = half_swap_sum(st.l[qb]);
-    const int qrow = qw0 + qb * 32 + c;
-    if (qrow < N) {
-      const float inv = 1.0f / lt;
-      bf16* orow = a.o + head + (size_t)qrow * D;
+    for (int db = 0; db < DB; db++)
 #pragma unroll
-      for (int db = 0; db < C::DB; db++) {
+      for (int g4 = 0; g4 < 4; g4++) {
+        bf16x4 ov;
 #pragma unroll
-        for (int g = 0; g < 4; g++) {
-          bf16x4 ov;
-#pragma unroll
-          for (int e = 0; e < 4; e++) ov[e] = (bf16)(st.acc[qb][db][4 * g + e] * inv);
-          *reinterpret_cast<bf16x4*>(orow + 32 * db + 8 * g + 4 * h) = ov;
-        }
+        for (int e = 0; e < 4; e++) ov[e] = (bf16)(st.acc[db][4 * g4 + e] * inv);
+        *reinterpret_cast<bf16x4*>(orow + 32 * db + 8 * g4 + 4 * L.h) = ov;
       }
-      if (h == 0) a.lse[(size_t)bh * N + qrow] = kLn2 * (st.m2[qb] + fast_log2(lt));
-    }
+    if (L.h == 0) a.lse[(size_t)bh * N + L.qrow] = kLn2 * (st.m2 + fast_log2(lt));
   }
 }
 
