@@ -68,8 +68,10 @@ def cpu_baseline(q, k, v, scale, causal, w, n_heads, budget_s=15.0):
     heads = [(b, h) for b in range(w["B"]) for h in range(w["H"])][:n_heads]
     dt = 0.0
     done = 0
+    group = w["H"] // w.get("H_kv", w["H"])  # query heads per K/V head
     for b, h in heads:
-        qh, kh, vh = (x[b, h].float().numpy().astype(np.float64) for x in (q, k, v))
+        qh = q[b, h].float().numpy().astype(np.float64)
+        kh, vh = (x[b, h // group].float().numpy().astype(np.float64) for x in (k, v))
         t0 = time.perf_counter()
         attention_head(qh, kh, vh, scale, causal)
         dt += time.perf_counter() - t0
@@ -131,14 +133,22 @@ def main():
     w = W.WORKLOADS[args.workload]
     causal = w["causal"][-1]
     q, k, v, scale = W.workload_inputs(args.workload)
+    layout = w.get("layout", "bhnd")
+    H_kv = w.get("H_kv", w["H"])
     dev = torch.device("cuda:0")
-    qd, kd, vd = (x.to(dev) for x in (q, k, v))
+    qd, kd, vd = (W.to_layout(x, layout).to(dev) for x in (q, k, v))
     o = torch.empty_like(qd)
     lse = torch.empty((w["B"], w["H"], w["N"]), dtype=torch.float32, device=dev)
     stream = torch.cuda.current_stream(dev)
-    fn = fa.fa_fwd if w["dtype"] == "bf16" else fa.fa_fwd_f32
-    argv = (qd.data_ptr(), kd.data_ptr(), vd.data_ptr(), o.data_ptr(), lse.data_ptr(),
-            w["B"], w["H"], w["N"], w["d"], scale, int(causal), stream.cuda_stream)
+    ptrs = (qd.data_ptr(), kd.data_ptr(), vd.data_ptr(), o.data_ptr(), lse.data_ptr())
+    if layout == "bhnd" and H_kv == w["H"]:
+        fn = fa.fa_fwd if w["dtype"] == "bf16" else fa.fa_fwd_f32
+        argv = ptrs + (w["B"], w["H"], w["N"], w["d"], scale, int(causal), stream.cuda_stream)
+    else:
+        fn = fa.fa_fwd_gqa if w["dtype"] == "bf16" else fa.fa_fwd_gqa_f32
+        lay = fa.FA_LAYOUT_BHND if layout == "bhnd" else fa.FA_LAYOUT_BNHD
+        argv = ptrs + (w["B"], w["H"], H_kv, w["N"], w["d"], scale, int(causal), lay,
+                       stream.cuda_stream)
 
     def step():
         rc = fn(*argv)
@@ -179,9 +189,9 @@ def main():
         "vs_baseline": None,
         "dtype": w["dtype"],
         "data": "synthetic (seeded N(0,1) Q, K, V)",
-        "config": {"workload": args.workload, "B": w["B"], "H": w["H"], "N": w["N"],
-                   "d": w["d"], "causal": causal, "kernel": "fa_fwd" if w["dtype"] == "bf16"
-                   else "fa_fwd_f32"},
+        "config": {"workload": args.workload, "B": w["B"], "H": w["H"], "H_kv": H_kv,
+                   "N": w["N"], "d": w["d"], "causal": causal, "layout": layout,
+                   "kernel": fn.__name__},
         "roofline": {"bound": "mfma" if w["dtype"] == "bf16" else "alu",
                      "achieved": round(tflops, 2), "peak": peak, "unit": "TFLOP/s",
                      "frac": round(tflops / peak, 4), "traffic": recorded_traffic(args.workload)},

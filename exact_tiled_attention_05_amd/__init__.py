@@ -9,24 +9,30 @@ is missing the calls raise.
 Raw entry points (same names and argument order as the C-ABI; pointers are integers):
     fa_fwd(q, k, v, o, lse, B, H, N, d, scale, causal, stream) -> int
     fa_fwd_f32(q, k, v, o, lse, B, H, N, d, scale, causal, stream) -> int
+    fa_fwd_gqa(q, k, v, o, lse, B, H, H_kv, N, d, scale, causal, layout, stream) -> int
+    fa_fwd_gqa_f32(q, k, v, o, lse, B, H, H_kv, N, d, scale, causal, layout, stream) -> int
     fa_strerror(code) -> str
     fa_version() -> int
 Tensor convenience (PyTorch supplies device memory and the stream):
-    forward(q, k, v, scale=None, causal=False, out=None, lse=None) -> (o, lse)
+    forward(q, k, v, scale=None, causal=False, out=None, lse=None, stream=None, layout="bhnd")
+        -> (o, lse)
 """
 import ctypes
 import math
 import os
 
-__all__ = ["fa_fwd", "fa_fwd_f32", "fa_strerror", "fa_version", "forward", "FAError",
-           "library_path", "load_library", "FA_OK", "FA_ERR_INVALID_ARG", "FA_ERR_UNSUPPORTED",
-           "FA_ERR_ALIGNMENT", "FA_ERR_LAUNCH"]
+__all__ = ["fa_fwd", "fa_fwd_f32", "fa_fwd_gqa", "fa_fwd_gqa_f32", "fa_strerror", "fa_version",
+           "forward", "FAError", "library_path", "load_library", "FA_OK", "FA_ERR_INVALID_ARG",
+           "FA_ERR_UNSUPPORTED", "FA_ERR_ALIGNMENT", "FA_ERR_LAUNCH", "FA_LAYOUT_BHND",
+           "FA_LAYOUT_BNHD"]
 
 FA_OK = 0
 FA_ERR_INVALID_ARG = -1
 FA_ERR_UNSUPPORTED = -2
 FA_ERR_ALIGNMENT = -3
 FA_ERR_LAUNCH = -4
+FA_LAYOUT_BHND = 0
+FA_LAYOUT_BNHD = 1
 
 _HERE = os.path.dirname(os.path.abspath(__file__))
 _LIB = None
@@ -53,9 +59,12 @@ def load_library():
         lib = ctypes.CDLL(path)
         fwd_args = [ctypes.c_void_p] * 5 + [ctypes.c_int] * 4 + [ctypes.c_float, ctypes.c_int,
                                                                    ctypes.c_void_p]
-        for name in ("fa_fwd", "fa_fwd_f32"):
+        gqa_args = [ctypes.c_void_p] * 5 + [ctypes.c_int] * 5 + [ctypes.c_float, ctypes.c_int,
+                                                                   ctypes.c_int, ctypes.c_void_p]
+        for name, argt in (("fa_fwd", fwd_args), ("fa_fwd_f32", fwd_args),
+                           ("fa_fwd_gqa", gqa_args), ("fa_fwd_gqa_f32", gqa_args)):
             fn = getattr(lib, name)
-            fn.argtypes = fwd_args
+            fn.argtypes = argt
             fn.restype = ctypes.c_int
         lib.fa_strerror.argtypes = [ctypes.c_int]
         lib.fa_strerror.restype = ctypes.c_char_p
@@ -73,6 +82,16 @@ def fa_fwd_f32(q, k, v, o, lse, B, H, N, d, scale, causal, stream=None):
     return load_library().fa_fwd_f32(q, k, v, o, lse, B, H, N, d, scale, causal, stream)
 
 
+def fa_fwd_gqa(q, k, v, o, lse, B, H, H_kv, N, d, scale, causal, layout, stream=None):
+    return load_library().fa_fwd_gqa(q, k, v, o, lse, B, H, H_kv, N, d, scale, causal, layout,
+                                     stream)
+
+
+def fa_fwd_gqa_f32(q, k, v, o, lse, B, H, H_kv, N, d, scale, causal, layout, stream=None):
+    return load_library().fa_fwd_gqa_f32(q, k, v, o, lse, B, H, H_kv, N, d, scale, causal,
+                                         layout, stream)
+
+
 def fa_strerror(code):
     return load_library().fa_strerror(code).decode()
 
@@ -81,23 +100,36 @@ def fa_version():
     return load_library().fa_version()
 
 
-def forward(q, k, v, scale=None, causal=False, out=None, lse=None, stream=None):
-    """Attention forward on [B, H, N, d] CUDA/HIP tensors (bf16 or fp32, contiguous).
+def forward(q, k, v, scale=None, causal=False, out=None, lse=None, stream=None, layout="bhnd"):
+    """Attention forward on CUDA/HIP tensors (bf16 or fp32, contiguous).
 
-    Returns (o, lse) with o like q and lse float32 [B, H, N]. ``out``/``lse`` may be passed to
-    reuse buffers; ``stream`` defaults to torch's current stream on q's device.
+    layout "bhnd": q [B, H, N, d], k and v [B, H_kv, N, d]; layout "bnhd": q [B, N, H, d], k and
+    v [B, N, H_kv, d]. H must be a multiple of H_kv (query head h uses K/V head h // (H // H_kv);
+    H_kv = H is ordinary multi-head attention). Returns (o, lse) with o like q and lse float32
+    [B, H, N]. ``out``/``lse`` may be passed to reuse buffers; ``stream`` defaults to torch's
+    current stream on q's device.
     """
     import torch
 
-    if q.dim() != 4 or k.shape != q.shape or v.shape != q.shape:
-        raise ValueError("q, k, v must all be [B, H, N, d] with the same shape")
+    if layout not in ("bhnd", "bnhd"):
+        raise ValueError("layout must be 'bhnd' or 'bnhd'")
+    if q.dim() != 4 or k.dim() != 4 or k.shape != v.shape:
+        raise ValueError("q, k, v must be 4-D and k, v must have the same shape")
+    if layout == "bhnd":
+        B, H, N, d = q.shape
+        Bk, H_kv, Nk, dk = k.shape
+    else:
+        B, N, H, d = q.shape
+        Bk, Nk, H_kv, dk = k.shape
+    if (Bk, Nk, dk) != (B, N, d) or H_kv < 1 or H % H_kv != 0:
+        raise ValueError("k, v must match q in batch, length and head dim, with H a multiple of "
+                         "their head count")
     if not (q.dtype == k.dtype == v.dtype) or q.dtype not in (torch.bfloat16, torch.float32):
         raise ValueError("q, k, v must all be bfloat16 or all float32")
     if not (q.is_cuda and k.device == q.device and v.device == q.device):
         raise ValueError("q, k, v must be on the same GPU device")
     if not (q.is_contiguous() and k.is_contiguous() and v.is_contiguous()):
         raise ValueError("q, k, v must be contiguous")
-    B, H, N, d = q.shape
     if scale is None:
         scale = 1.0 / math.sqrt(d)
     if out is None:
@@ -112,9 +144,14 @@ def forward(q, k, v, scale=None, causal=False, out=None, lse=None, stream=None):
         raise ValueError("lse must be a contiguous float32 [B, H, N] tensor on q's device")
     if stream is None:
         stream = torch.cuda.current_stream(q.device).cuda_stream
-    fn = fa_fwd if q.dtype == torch.bfloat16 else fa_fwd_f32
-    rc = fn(q.data_ptr(), k.data_ptr(), v.data_ptr(), out.data_ptr(), lse.data_ptr(),
-            B, H, N, d, float(scale), int(bool(causal)), stream)
+    ptrs = (q.data_ptr(), k.data_ptr(), v.data_ptr(), out.data_ptr(), lse.data_ptr())
+    if layout == "bhnd" and H_kv == H:
+        fn = fa_fwd if q.dtype == torch.bfloat16 else fa_fwd_f32
+        rc = fn(*ptrs, B, H, N, d, float(scale), int(bool(causal)), stream)
+    else:
+        fn = fa_fwd_gqa if q.dtype == torch.bfloat16 else fa_fwd_gqa_f32
+        lay = FA_LAYOUT_BHND if layout == "bhnd" else FA_LAYOUT_BNHD
+        rc = fn(*ptrs, B, H, H_kv, N, d, float(scale), int(bool(causal)), lay, stream)
     if rc != FA_OK:
         raise FAError(rc, fn.__name__)
     return out, lse

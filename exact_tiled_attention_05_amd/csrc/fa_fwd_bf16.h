@@ -62,6 +62,10 @@ namespace fa {
 
 constexpr float kRescaleSlack = 2.0f;
 
+// Shapes and strides. Query head h of batch b reads K/V head h / group ("Understanding
+// FlashAttention Pt 1", §4.1: the query heads divide evenly over the K/V heads and each attends
+// with its assigned one; MHA is group 1, MQA one K/V head). q and o share one set of element
+// strides, k and v another; lse is always [B][H][N].
 struct Bf16Args {
   const bf16* q;
   const bf16* k;
@@ -69,9 +73,14 @@ struct Bf16Args {
   bf16* o;
   float* lse;
   int N;             // sequence length
-  int BH;            // batch * heads
+  int BH;            // batch * query heads
+  int H;             // query heads
+  int group;         // query heads per K/V head
   int n_qblk;        // query blocks per head
   float scale_log2;  // scale * log2(e)
+  long long q_bs, q_hs;    // q/o element strides of a batch and a head
+  long long kv_bs, kv_hs;  // k/v element strides of a batch and a head
+  int q_rs, kv_rs;         // element strides of a row (one token)
 };
 
 constexpr int kNumWaves = 8;                    // waves per workgroup
@@ -104,19 +113,36 @@ struct TileRegs {
   u32x4 k[LOADS], v[LOADS];
 };
 
-// Loads go through raw buffer resources: piece i of wave w is the 1 KB at byte
-// key0 * 2D + (i * 8 + w) * 1024 of the head, lane L's 16 bytes at +16 L. The per-lane part of the
-// offset is the same for every piece and tile and the rest is scalar, so a load costs no vector
-// ALU work. Rows at or past N lie past the buffer's size and read as zeros (their scores are
-// masked).
+// Loads go through raw buffer resources laid over the tile's rows: a resource starts at the
+// tile's first row and ends after its last row below N, so rows at or past N read as zeros
+// (their scores are masked) and every offset stays small whatever the row stride. Piece i of
+// wave w holds rows (i * 8 + w) * R .. + R - 1 of the tile (R = 64 / (D/8) rows per piece); lane
+// L's 16 bytes are chunk L % (D/8) of row L / (D/8). The per-lane offset (voff) is the same for
+// every piece and tile and the piece offset is scalar, so a load costs no vector ALU work.
 template <int D>
-__device__ __forceinline__ void load_tile(__amdgpu_buffer_rsrc_t rk, __amdgpu_buffer_rsrc_t rv,
-                                          int key0, int wave, int lane, TileRegs<D>& r) {
+struct TileSrc {
+  const char* kbase;  // byte address of row 0 of this head's K (V at the same offsets from vbase)
+  const char* vbase;
+  long long rs;       // bytes between consecutive rows
+  int voff;           // this lane's byte offset inside a piece
+};
+
+template <int D>
+__device__ __forceinline__ void load_tile(const TileSrc<D>& src, int key0, int N, int wave,
+                                          TileRegs<D>& r) {
+  constexpr int CPR = D / 8, RPP = 64 / CPR;
+  const long long t0 = (long long)key0 * src.rs;
+  const int rows = min(N - key0, kBlockK);  // >= 1: only tiles that start below N are loaded
+  const int bytes = (int)((rows - 1) * src.rs) + 2 * D;
+  const __amdgpu_buffer_rsrc_t rk =
+      __builtin_amdgcn_make_buffer_rsrc((void*)(src.kbase + t0), 0, bytes, 0x00020000);
+  const __amdgpu_buffer_rsrc_t rv =
+      __builtin_amdgcn_make_buffer_rsrc((void*)(src.vbase + t0), 0, bytes, 0x00020000);
 #pragma unroll
   for (int i = 0; i < TileRegs<D>::LOADS; i++) {
-    const int soff = key0 * (2 * D) + (i * kNumWaves + wave) * 1024;
-    r.k[i] = __builtin_bit_cast(u32x4, __builtin_amdgcn_raw_buffer_load_b128(rk, 16 * lane, soff, 0));
-    r.v[i] = __builtin_bit_cast(u32x4, __builtin_amdgcn_raw_buffer_load_b128(rv, 16 * lane, soff, 0));
+    const int soff = (int)((i * kNumWaves + wave) * RPP * src.rs);
+    r.k[i] = __builtin_bit_cast(u32x4, __builtin_amdgcn_raw_buffer_load_b128(rk, src.voff, soff, 0));
+    r.v[i] = __builtin_bit_cast(u32x4, __builtin_amdgcn_raw_buffer_load_b128(rv, src.voff, soff, 0));
   }
 }
 
@@ -277,13 +303,17 @@ __global__ __launch_bounds__(kNumWaves * 64) void fa_fwd_bf16_kernel(Bf16Args a)
 
   int bh, qblk;
   map_block<CAUSAL>(blockIdx.x, gridDim.x, a.BH, a.n_qblk, bh, qblk);
-  const size_t head = (size_t)bh * N * D;
-  const bf16* __restrict__ Qh = a.q + head;
-  // N * D * 2 <= 2^30 for N <= 2^22 and D <= 128
-  const __amdgpu_buffer_rsrc_t rk =
-      __builtin_amdgcn_make_buffer_rsrc((void*)(a.k + head), 0, N * D * 2, 0x00020000);
-  const __amdgpu_buffer_rsrc_t rv =
-      __builtin_amdgcn_make_buffer_rsrc((void*)(a.v + head), 0, N * D * 2, 0x00020000);
+  const int b = bh / a.H, h = bh - b * a.H, hk = h / a.group;
+  const long long qhead = b * a.q_bs + h * a.q_hs;  // element offset of this head's row 0
+  const bf16* __restrict__ Qh = a.q + qhead;
+  TileSrc<D> src;
+  {
+    const long long kvhead = b * a.kv_bs + hk * a.kv_hs;
+    src.kbase = reinterpret_cast<const char*>(a.k + kvhead);
+    src.vbase = reinterpret_cast<const char*>(a.v + kvhead);
+    src.rs = 2LL * a.kv_rs;
+    src.voff = (int)((lane / (D / 8)) * src.rs) + 16 * (lane % (D / 8));
+  }
   const int q0 = qblk * kBlockQ;
 
   Lane L;
@@ -315,19 +345,19 @@ __global__ __launch_bounds__(kNumWaves * 64) void fa_fwd_bf16_kernel(Bf16Args a)
 
   // Prologue: tile 0 into stage 0, Q into registers, tile 1 into the staging registers, S(0).
   TileRegs<D> stage;
-  load_tile<D>(rk, rv, 0, wave, lane, stage);
+  load_tile<D>(src, 0, N, wave, stage);
   WaveState<D> st;
 #pragma unroll
   for (int dk = 0; dk < DK; dk++)
     st.qf[dk] = (L.qrow < N)
-                    ? *reinterpret_cast<const bf16x8*>(Qh + (size_t)L.qrow * D + dk * 16 + L.h * 8)
+                    ? *reinterpret_cast<const bf16x8*>(Qh + (long long)L.qrow * a.q_rs + dk * 16 + L.h * 8)
                     : bf16x8{};
 #pragma unroll
   for (int db = 0; db < DB; db++) st.acc[db] = f32x16{};
   st.m2 = -INFINITY;
   st.l = 0.f;
   store_tile<D>(sK0, sV0, wave, lane, stage);
-  if (n_kt > 1) load_tile<D>(rk, rv, kBlockK, wave, lane, stage);
+  if (n_kt > 1) load_tile<D>(src, kBlockK, N, wave, stage);
   __syncthreads();
   st.s = f32x16{};
   if (L.last >= 0) {
@@ -341,7 +371,7 @@ __global__ __launch_bounds__(kNumWaves * 64) void fa_fwd_bf16_kernel(Bf16Args a)
   auto crossing = [&](char* __restrict__ Kn, char* __restrict__ Vn, int j) {
     store_tile<D>(Kn, Vn, wave, lane, stage);
     __syncthreads();
-    if (j + 2 < n_kt) load_tile<D>(rk, rv, (j + 2) * kBlockK, wave, lane, stage);
+    if (j + 2 < n_kt) load_tile<D>(src, (j + 2) * kBlockK, N, wave, stage);
   };
 
   // Tile j in stage S (a compile-time constant, so every LDS address is a base plus an immediate
@@ -396,7 +426,7 @@ __global__ __launch_bounds__(kNumWaves * 64) void fa_fwd_bf16_kernel(Bf16Args a)
   const float lt = half_swap_sum(st.l);
   if (L.qrow < N) {
     const float inv = 1.0f / lt;
-    bf16* orow = a.o + head + (size_t)L.qrow * D;
+    bf16* orow = a.o + qhead + (long long)L.qrow * a.q_rs;
 #pragma unroll
     for (int db = 0; db < DB; db++)
 #pragma unroll

@@ -14,6 +14,7 @@
 
 namespace fa {
 
+// Same shapes, head grouping and strides as Bf16Args (fa_fwd_bf16.h).
 struct F32Args {
   const float* q;
   const float* k;
@@ -22,7 +23,12 @@ struct F32Args {
   float* lse;
   int N;
   int BH;
+  int H;
+  int group;
   float scale_log2;
+  long long q_bs, q_hs;
+  long long kv_bs, kv_hs;
+  int q_rs, kv_rs;
 };
 
 constexpr int kF32BlockQ = 128;
@@ -38,15 +44,17 @@ __global__ __launch_bounds__(kF32BlockQ) void fa_fwd_f32_kernel(F32Args a) {
   const int qblk = CAUSAL ? (gridDim.x - 1 - blockIdx.x) : blockIdx.x;
   const int q0 = qblk * kF32BlockQ;
   const int qrow = q0 + threadIdx.x;
-  const size_t head = (size_t)bh * N * D;
-  const float* Qh = a.q + head;
-  const float* Kh = a.k + head;
-  const float* Vh = a.v + head;
+  const int b = bh / a.H, h = bh - b * a.H, hk = h / a.group;
+  const long long qhead = b * a.q_bs + h * a.q_hs;
+  const long long kvhead = b * a.kv_bs + hk * a.kv_hs;
+  const float* Qh = a.q + qhead;
+  const float* Kh = a.k + kvhead;
+  const float* Vh = a.v + kvhead;
 
   float qr[D], o[D];
 #pragma unroll
   for (int t = 0; t < D; t++) {
-    qr[t] = (qrow < N) ? Qh[(size_t)qrow * D + t] : 0.f;
+    qr[t] = (qrow < N) ? Qh[(long long)qrow * a.q_rs + t] : 0.f;
     o[t] = 0.f;
   }
   float m2 = -INFINITY, l = 0.f;
@@ -58,8 +66,8 @@ __global__ __launch_bounds__(kF32BlockQ) void fa_fwd_f32_kernel(F32Args a) {
     for (int e = threadIdx.x; e < kF32BlockK * D; e += kF32BlockQ) {
       const int r = e / D, t = e % D;
       const bool in = k0 + r < N;
-      Ks[r][t] = in ? Kh[(size_t)(k0 + r) * D + t] : 0.f;
-      Vs[r][t] = in ? Vh[(size_t)(k0 + r) * D + t] : 0.f;
+      Ks[r][t] = in ? Kh[(long long)(k0 + r) * a.kv_rs + t] : 0.f;
+      Vs[r][t] = in ? Vh[(long long)(k0 + r) * a.kv_rs + t] : 0.f;
     }
     __syncthreads();
     const int kend = min(kF32BlockK, n_keys - k0);
@@ -86,10 +94,10 @@ __global__ __launch_bounds__(kF32BlockQ) void fa_fwd_f32_kernel(F32Args a) {
 
   if (qrow < N) {
     const float inv = 1.0f / l;
-    float* orow = a.o + head + (size_t)qrow * D;
+    float* orow = a.o + qhead + (long long)qrow * a.q_rs;
 #pragma unroll
     for (int t = 0; t < D; t++) orow[t] = o[t] * inv;
-    a.lse[(size_t)bh * N + qrow] = kLn2 * (m2 + log2f(l));
+    a.lse[(long long)bh * N + qrow] = kLn2 * (m2 + log2f(l));
   }
 }
 

@@ -14,7 +14,9 @@ The five workloads are the shapes the pages discuss: a single small head, a mid-
 d = 64, the Llama-3-8B layer shape (32 heads at N = 8192, d = 128, causal) that the
 "FlashAttention-2 -- Deeper Math" page uses for its occupancy argument (Fix 4) and that
 "Flash Attention" ("The problem, quantified") uses for its traffic count, a large-score stress
-case, and a 32K-token causal case.
+case, and a 32K-token causal case. A sixth gives that Llama layer its grouped K/V heads (32 query
+heads over 8 K/V heads, "Understanding FlashAttention Pt 1", §4.1) in the tokens-outermost
+[B][N][heads][d] layout of that section; K and V are then drawn with H_kv heads.
 """
 import math
 
@@ -29,6 +31,8 @@ WORKLOADS = {
                                q_mult=8.0, outlier_frac=0.01, outlier_mult=4.0),
     "long_n32k_causal": dict(B=1, H=32, N=32768, d=128, dtype="bf16", causal=(True,), seed=4,
                              sample_rows=64),
+    "llama3_8b_gqa_n8k_causal": dict(B=1, H=32, H_kv=8, N=8192, d=128, dtype="bf16",
+                                     causal=(True,), seed=5, layout="bnhd", sample_rows=64),
 }
 
 _TORCH_DTYPE = {"bf16": torch.bfloat16, "fp32": torch.float32}
@@ -58,22 +62,33 @@ def outlier_rows(N, count, seed):
 
 
 def make_inputs(B, H, N, d, dtype="bf16", seed=0, q_mult=1.0, outlier_frac=0.0,
-                outlier_mult=4.0, **_ignored):
-    """Return (q, k, v) CPU tensors of shape [B, H, N, d] in the compute dtype."""
+                outlier_mult=4.0, H_kv=None, **_ignored):
+    """Return (q, k, v) CPU tensors in the compute dtype: q [B, H, N, d], k and v [B, H_kv, N, d]
+    (H_kv defaults to H)."""
+    H_kv = H if H_kv is None else H_kv
     g = torch.Generator().manual_seed(seed)
     q = torch.randn((B, H, N, d), generator=g, dtype=torch.float32)
-    k = torch.randn((B, H, N, d), generator=g, dtype=torch.float32)
-    v = torch.randn((B, H, N, d), generator=g, dtype=torch.float32)
+    k = torch.randn((B, H_kv, N, d), generator=g, dtype=torch.float32)
+    v = torch.randn((B, H_kv, N, d), generator=g, dtype=torch.float32)
     if q_mult != 1.0:
         q.mul_(q_mult)
     if outlier_frac > 0.0:
         count = max(1, int(math.floor(outlier_frac * N)))
         for b in range(B):
-            for h in range(H):
+            for h in range(H_kv):
                 idx = outlier_rows(N, count, seed * 1000003 + b * 4099 + h)
                 k[b, h, idx] *= outlier_mult
     t = _TORCH_DTYPE[dtype]
     return q.to(t).contiguous(), k.to(t).contiguous(), v.to(t).contiguous()
+
+
+def to_layout(x, layout):
+    """A [B, heads, N, d] tensor as a contiguous tensor in the given layout ("bhnd" or "bnhd")."""
+    if layout == "bhnd":
+        return x.contiguous()
+    if layout == "bnhd":
+        return x.permute(0, 2, 1, 3).contiguous()
+    raise ValueError("layout must be 'bhnd' or 'bnhd'")
 
 
 def sampled_rows(N, count, seed):

@@ -34,6 +34,15 @@
  *     cross-workgroup reductions).
  *   - Thread-safe: no global mutable state.
  *   - Limits: 1 <= N <= 2^22 and 1 <= B*H <= 65535.
+ *
+ * Grouped K/V heads ("Understanding FlashAttention Pt 1", §4.1): fa_fwd_gqa and fa_fwd_gqa_f32
+ * take H query heads and H_kv key/value heads with H a multiple of H_kv. Query head h attends with
+ * K/V head h / (H / H_kv), so consecutive groups of H / H_kv query heads share one K/V head:
+ * H_kv = H is ordinary multi-head attention, H_kv = 1 is multi-query attention. They also take a
+ * layout for q, k, v and o (lse stays [B][H][N]):
+ *   FA_LAYOUT_BHND  q, o [B][H][N][d]     k, v [B][H_kv][N][d]   (the layout of fa_fwd)
+ *   FA_LAYOUT_BNHD  q, o [B][N][H][d]     k, v [B][N][H_kv][d]   (tokens outermost, as in §4.1)
+ * Each layout is contiguous row-major; every other convention above applies unchanged.
  */
 #ifndef FA_H_
 #define FA_H_
@@ -48,6 +57,9 @@ extern "C" {
 #define FA_ERR_UNSUPPORTED (-2) /* head dim d not in {64, 128} */
 #define FA_ERR_ALIGNMENT (-3)   /* a pointer is not 16-byte aligned */
 #define FA_ERR_LAUNCH (-4)      /* the kernel launch call returned an error */
+
+#define FA_LAYOUT_BHND 0 /* [B][heads][N][d] */
+#define FA_LAYOUT_BNHD 1 /* [B][N][heads][d] */
 
 /*
  * fa_fwd -- bf16 inputs and outputs, fp32 arithmetic for the softmax and both accumulations.
@@ -67,6 +79,22 @@ int fa_fwd(const void* q, const void* k, const void* v, void* o, float* lse,
  */
 int fa_fwd_f32(const float* q, const float* k, const float* v, float* o, float* lse,
                int B, int H, int N, int d, float scale, int causal, void* stream);
+
+/*
+ * fa_fwd_gqa -- fa_fwd with H_kv key/value heads (H a multiple of H_kv) and a layout
+ * (FA_LAYOUT_BHND or FA_LAYOUT_BNHD) for q, k, v, o. k and v hold B*H_kv*N*d elements, q and o
+ * B*H*N*d, lse B*H*N floats. H_kv < 1, H not a multiple of H_kv or an unknown layout return
+ * FA_ERR_INVALID_ARG. fa_fwd(q,k,v,o,lse,B,H,N,d,s,c,st) is fa_fwd_gqa(..., B, H, H, N, d, s, c,
+ * FA_LAYOUT_BHND, st).
+ */
+int fa_fwd_gqa(const void* q, const void* k, const void* v, void* o, float* lse,
+               int B, int H, int H_kv, int N, int d, float scale, int causal, int layout,
+               void* stream);
+
+/* fa_fwd_gqa_f32 -- the fp32 counterpart of fa_fwd_gqa (as fa_fwd_f32 is of fa_fwd). */
+int fa_fwd_gqa_f32(const float* q, const float* k, const float* v, float* o, float* lse,
+                   int B, int H, int H_kv, int N, int d, float scale, int causal, int layout,
+                   void* stream);
 
 /* Human-readable text for a return code (static storage; never NULL). */
 const char* fa_strerror(int code);

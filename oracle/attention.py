@@ -92,3 +92,44 @@ def attention(q, k, v, scale, causal=False, rows=None):
                 r = ra if ra.ndim == 1 else ra[b, h]
             o[b, h], lse[b, h] = attention_head(q[b, h], k[b, h], v[b, h], scale, causal, r)
     return o, lse
+
+
+def kv_head_of(h, H, H_kv):
+    """K/V head that query head h attends with.
+
+    "Understanding FlashAttention Pt 1", §4.1: the number of query heads is a multiple of the
+    number of K/V heads and each query head is evaluated against its assigned K/V head (one per
+    query head for MHA, a single shared one for MQA). The page does not spell the assignment out;
+    the reading used here is the grouped one: the H query heads form H_kv consecutive groups of
+    H / H_kv heads, and group j uses K/V head j.
+    """
+    if H_kv < 1 or H % H_kv != 0:
+        raise ValueError("the query heads must divide evenly over the K/V heads")
+    return h // (H // H_kv)
+
+
+def attention_gqa(q, k, v, scale, causal=False, rows=None):
+    """Batched naive attention with grouped K/V heads ("Understanding FlashAttention Pt 1", §4.1).
+
+    q: [B, H, N, d]; k, v: [B, H_kv, N, d] with H a multiple of H_kv. Query head h attends with
+    K/V head kv_head_of(h, H, H_kv); everything else is attention_head. rows as in attention().
+    Returns (O [B, H, R, dv], LSE [B, H, R]) in float64.
+    """
+    q = np.asarray(q)
+    k = np.asarray(k)
+    v = np.asarray(v)
+    B, H = q.shape[0], q.shape[1]
+    H_kv = k.shape[1]
+    R = q.shape[2] if rows is None else np.asarray(rows).shape[-1]
+    o = np.empty((B, H, R, v.shape[3]), dtype=np.float64)
+    lse = np.empty((B, H, R), dtype=np.float64)
+    for b in range(B):
+        for h in range(H):
+            j = kv_head_of(h, H, H_kv)
+            if rows is None:
+                r = None
+            else:
+                ra = np.asarray(rows)
+                r = ra if ra.ndim == 1 else ra[b, h]
+            o[b, h], lse[b, h] = attention_head(q[b, h], k[b, j], v[b, j], scale, causal, r)
+    return o, lse

@@ -66,3 +66,40 @@ def compare(o_gpu, lse_gpu, ref):
         eo = max(eo, float(np.abs(o_gpu[b, h, r] - o).max()))
         el = max(el, float(np.abs(lse_gpu[b, h, r] - lse).max()))
     return eo, el
+
+
+def run_gpu_layout(q, k, v, scale, causal, layout):
+    """Like run_gpu for [B, H, N, d] / [B, H_kv, N, d] CPU tensors, but hands the GPU copies in
+    ``layout`` ("bhnd" or "bnhd") and returns O back in [B, H, N, d] order."""
+    from exact_tiled_attention_05_amd.workloads import to_layout
+    dev = torch.device("cuda:0")
+    qd, kd, vd = (to_layout(x, layout).to(dev) for x in (q, k, v))
+    o, lse = fa.forward(qd, kd, vd, scale=scale, causal=causal, layout=layout)
+    torch.cuda.synchronize()
+    if layout == "bnhd":
+        o = o.permute(0, 2, 1, 3)
+    return o.float().cpu().numpy().astype(np.float64), lse.cpu().numpy().astype(np.float64)
+
+
+def oracle_rows_gqa(q, k, v, scale, causal, rows=None, heads=None, workers=None):
+    """oracle_rows for grouped K/V heads: query head h uses the K/V head the oracle assigns it."""
+    from oracle import kv_head_of
+    B, H, N, _ = q.shape
+    H_kv = k.shape[1]
+    if heads is None:
+        heads = [(b, h) for b in range(B) for h in range(H)]
+
+    def one(bh):
+        b, h = bh
+        j = kv_head_of(h, H, H_kv)
+        r = rows.get(bh) if isinstance(rows, dict) else rows
+        r = np.arange(N) if r is None else np.asarray(r)
+        o, lse = attention_head(_as64(q[b, h]), _as64(k[b, j]), _as64(v[b, j]), scale, causal, r)
+        return bh, (r, o, lse)
+
+    workers = workers or min(16, os.cpu_count() or 1)
+    out = {}
+    with cf.ThreadPoolExecutor(max_workers=workers) as ex:
+        for bh, res in ex.map(one, heads):
+            out[bh] = res
+    return out

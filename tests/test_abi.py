@@ -26,7 +26,8 @@ def _codes():
 
 
 def test_header_declares_the_expected_entry_points():
-    assert _declared() == ["fa_fwd", "fa_fwd_f32", "fa_strerror", "fa_version"]
+    assert _declared() == ["fa_fwd", "fa_fwd_f32", "fa_fwd_gqa", "fa_fwd_gqa_f32", "fa_strerror",
+                           "fa_version"]
 
 
 def test_library_exports_every_declared_symbol():
@@ -94,6 +95,39 @@ def test_bad_arguments_are_refused(fn_name, kw, code):
     assert _call(getattr(fa, fn_name), **kw) == code
 
 
+GOOD_GQA = dict(GOOD, H=4, H_kv=2, layout=fa.FA_LAYOUT_BNHD)
+
+
+def _call_gqa(fn, **kw):
+    a = dict(GOOD_GQA, **kw)
+    return fn(a["q"], a["k"], a["v"], a["o"], a["lse"], a["B"], a["H"], a["H_kv"], a["N"], a["d"],
+              a["scale"], a["causal"], a["layout"], None)
+
+
+BAD_GQA = [(kw, code) for kw, code in BAD if "H" not in kw] + [
+    (dict(H_kv=0), fa.FA_ERR_INVALID_ARG),
+    (dict(H_kv=-2), fa.FA_ERR_INVALID_ARG),
+    (dict(H_kv=3), fa.FA_ERR_INVALID_ARG),          # 4 query heads do not split over 3
+    (dict(H_kv=8), fa.FA_ERR_INVALID_ARG),          # more K/V heads than query heads
+    (dict(layout=2), fa.FA_ERR_INVALID_ARG),
+    (dict(layout=-1), fa.FA_ERR_INVALID_ARG),
+    (dict(H=256, H_kv=1, B=256), fa.FA_ERR_INVALID_ARG),
+]
+
+
+@pytest.mark.parametrize("fn_name", ["fa_fwd_gqa", "fa_fwd_gqa_f32"])
+@pytest.mark.parametrize("kw,code", BAD_GQA, ids=[str(b[0]) for b in BAD_GQA])
+def test_bad_gqa_arguments_are_refused(fn_name, kw, code):
+    assert _call_gqa(getattr(fa, fn_name), **kw) == code
+
+
+def test_gqa_overlap_uses_kv_sizes():
+    """k and v hold B*H_kv*N*d elements: an o placed right after a (smaller) k is accepted by the
+    checks only if it does not overlap; one element into k is refused."""
+    kv_bytes = 2 * 2 * 100 * 64 * 2  # B*H_kv*N*d bf16
+    assert _call_gqa(fa.fa_fwd_gqa, o=K + kv_bytes - 16) == fa.FA_ERR_INVALID_ARG
+
+
 def test_forward_checks_tensors_before_any_gpu_use():
     q = torch.zeros(1, 1, 8, 64, dtype=torch.bfloat16)
     with pytest.raises(ValueError):
@@ -104,3 +138,17 @@ def test_forward_checks_tensors_before_any_gpu_use():
         fa.forward(q[0], q[0], q[0])  # not 4-D
     with pytest.raises(ValueError):
         fa.forward(q.half(), q.half(), q.half())  # fp16 is not a supported dtype
+
+
+def test_forward_checks_gqa_shapes_before_any_gpu_use():
+    q = torch.zeros(1, 4, 8, 64, dtype=torch.bfloat16)
+    k3 = torch.zeros(1, 3, 8, 64, dtype=torch.bfloat16)
+    with pytest.raises(ValueError):
+        fa.forward(q, k3, k3)  # 4 query heads do not split over 3 K/V heads
+    with pytest.raises(ValueError):
+        fa.forward(q, q, q, layout="nhbd")  # unknown layout
+    k = torch.zeros(1, 2, 8, 64, dtype=torch.bfloat16)
+    with pytest.raises(ValueError):
+        fa.forward(q, k, torch.zeros(1, 2, 9, 64, dtype=torch.bfloat16))  # k, v differ
+    with pytest.raises(ValueError):
+        fa.forward(q, k, k)  # CPU tensors (shapes are fine)
