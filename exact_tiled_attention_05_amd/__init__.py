@@ -11,18 +11,23 @@ Raw entry points (same names and argument order as the C-ABI; pointers are integ
     fa_fwd_f32(q, k, v, o, lse, B, H, N, d, scale, causal, stream) -> int
     fa_fwd_gqa(q, k, v, o, lse, B, H, H_kv, N, d, scale, causal, layout, stream) -> int
     fa_fwd_gqa_f32(q, k, v, o, lse, B, H, H_kv, N, d, scale, causal, layout, stream) -> int
+    fa_splitkv_workspace_bytes(B, H, H_kv, N_q, N_kv, d, causal, n_splits) -> int
+    fa_fwd_splitkv(q, k, v, o, lse, B, H, H_kv, N_q, N_kv, d, scale, causal, layout, n_splits,
+                   workspace, workspace_bytes, stream) -> int
     fa_strerror(code) -> str
     fa_version() -> int
 Tensor convenience (PyTorch supplies device memory and the stream):
     forward(q, k, v, scale=None, causal=False, out=None, lse=None, stream=None, layout="bhnd")
         -> (o, lse)
+    decode(q, k, v, scale=None, causal=False, layout="bhnd", n_splits=0, out=None, lse=None,
+           workspace=None, stream=None) -> (o, lse)
 """
 import ctypes
 import math
 import os
 
-__all__ = ["fa_fwd", "fa_fwd_f32", "fa_fwd_gqa", "fa_fwd_gqa_f32", "fa_strerror", "fa_version",
-           "forward", "FAError", "library_path", "load_library", "FA_OK", "FA_ERR_INVALID_ARG",
+__all__ = ["fa_fwd", "fa_fwd_f32", "fa_fwd_gqa", "fa_fwd_gqa_f32", "fa_fwd_splitkv",
+           "fa_splitkv_workspace_bytes", "fa_strerror", "fa_version", "forward", "decode", "FAError", "library_path", "load_library", "FA_OK", "FA_ERR_INVALID_ARG",
            "FA_ERR_UNSUPPORTED", "FA_ERR_ALIGNMENT", "FA_ERR_LAUNCH", "FA_LAYOUT_BHND",
            "FA_LAYOUT_BNHD"]
 
@@ -66,6 +71,12 @@ def load_library():
             fn = getattr(lib, name)
             fn.argtypes = argt
             fn.restype = ctypes.c_int
+        lib.fa_splitkv_workspace_bytes.argtypes = [ctypes.c_int] * 8
+        lib.fa_splitkv_workspace_bytes.restype = ctypes.c_size_t
+        lib.fa_fwd_splitkv.argtypes = ([ctypes.c_void_p] * 5 + [ctypes.c_int] * 6 +
+                                       [ctypes.c_float] + [ctypes.c_int] * 3 +
+                                       [ctypes.c_void_p, ctypes.c_size_t, ctypes.c_void_p])
+        lib.fa_fwd_splitkv.restype = ctypes.c_int
         lib.fa_strerror.argtypes = [ctypes.c_int]
         lib.fa_strerror.restype = ctypes.c_char_p
         lib.fa_version.argtypes = []
@@ -90,6 +101,16 @@ def fa_fwd_gqa(q, k, v, o, lse, B, H, H_kv, N, d, scale, causal, layout, stream=
 def fa_fwd_gqa_f32(q, k, v, o, lse, B, H, H_kv, N, d, scale, causal, layout, stream=None):
     return load_library().fa_fwd_gqa_f32(q, k, v, o, lse, B, H, H_kv, N, d, scale, causal,
                                          layout, stream)
+
+
+def fa_splitkv_workspace_bytes(B, H, H_kv, N_q, N_kv, d, causal, n_splits):
+    return load_library().fa_splitkv_workspace_bytes(B, H, H_kv, N_q, N_kv, d, causal, n_splits)
+
+
+def fa_fwd_splitkv(q, k, v, o, lse, B, H, H_kv, N_q, N_kv, d, scale, causal, layout, n_splits,
+                   workspace, workspace_bytes, stream=None):
+    return load_library().fa_fwd_splitkv(q, k, v, o, lse, B, H, H_kv, N_q, N_kv, d, scale, causal,
+                                         layout, n_splits, workspace, workspace_bytes, stream)
 
 
 def fa_strerror(code):
@@ -154,4 +175,56 @@ def forward(q, k, v, scale=None, causal=False, out=None, lse=None, stream=None, 
         rc = fn(*ptrs, B, H, H_kv, N, d, float(scale), int(bool(causal)), lay, stream)
     if rc != FA_OK:
         raise FAError(rc, fn.__name__)
+    return out, lse
+
+
+def decode(q, k, v, scale=None, causal=False, layout="bhnd", n_splits=0, out=None, lse=None,
+           workspace=None, stream=None):
+    """Split-KV attention of few queries against a long K/V sequence (bf16 CUDA/HIP tensors).
+
+    layout "bhnd": q [B, H, N_q, d], k and v [B, H_kv, N_kv, d]; "bnhd": q [B, N_q, H, d], k and
+    v [B, N_kv, H_kv, d]. Query i is token N_kv - N_q + i (causal: it sees keys up to there).
+    Returns (o, lse) with o like q and lse float32 [B, H, N_q]. ``workspace`` (a uint8 tensor of
+    at least fa_splitkv_workspace_bytes(...) bytes on q's device) is allocated here if not given.
+    """
+    import torch
+
+    if layout not in ("bhnd", "bnhd"):
+        raise ValueError("layout must be 'bhnd' or 'bnhd'")
+    if q.dim() != 4 or k.dim() != 4 or k.shape != v.shape:
+        raise ValueError("q, k, v must be 4-D and k, v must have the same shape")
+    if layout == "bhnd":
+        B, H, Nq, d = q.shape
+        Bk, H_kv, Nkv, dk = k.shape
+    else:
+        B, Nq, H, d = q.shape
+        Bk, Nkv, H_kv, dk = k.shape
+    if (Bk, dk) != (B, d) or H_kv < 1 or H % H_kv != 0:
+        raise ValueError("k, v must match q in batch and head dim, with H a multiple of their "
+                         "head count")
+    if not (q.dtype == k.dtype == v.dtype == torch.bfloat16):
+        raise ValueError("q, k, v must all be bfloat16")
+    if not (q.is_cuda and k.device == q.device and v.device == q.device):
+        raise ValueError("q, k, v must be on the same GPU device")
+    if not (q.is_contiguous() and k.is_contiguous() and v.is_contiguous()):
+        raise ValueError("q, k, v must be contiguous")
+    if scale is None:
+        scale = 1.0 / math.sqrt(d)
+    need = fa_splitkv_workspace_bytes(B, H, H_kv, Nq, Nkv, d, int(bool(causal)), n_splits)
+    if need == 0:
+        raise ValueError("shape not supported by split-KV decoding (see fa_fwd_splitkv limits)")
+    if out is None:
+        out = torch.empty_like(q)
+    if lse is None:
+        lse = torch.empty((B, H, Nq), dtype=torch.float32, device=q.device)
+    if workspace is None:
+        workspace = torch.empty(need, dtype=torch.uint8, device=q.device)
+    if stream is None:
+        stream = torch.cuda.current_stream(q.device).cuda_stream
+    lay = FA_LAYOUT_BHND if layout == "bhnd" else FA_LAYOUT_BNHD
+    rc = fa_fwd_splitkv(q.data_ptr(), k.data_ptr(), v.data_ptr(), out.data_ptr(), lse.data_ptr(),
+                        B, H, H_kv, Nq, Nkv, d, float(scale), int(bool(causal)), lay, n_splits,
+                        workspace.data_ptr(), workspace.numel() * workspace.element_size(), stream)
+    if rc != FA_OK:
+        raise FAError(rc, "fa_fwd_splitkv")
     return out, lse

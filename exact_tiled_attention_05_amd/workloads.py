@@ -16,7 +16,10 @@ d = 64, the Llama-3-8B layer shape (32 heads at N = 8192, d = 128, causal) that 
 "Flash Attention" ("The problem, quantified") uses for its traffic count, a large-score stress
 case, and a 32K-token causal case. A sixth gives that Llama layer its grouped K/V heads (32 query
 heads over 8 K/V heads, "Understanding FlashAttention Pt 1", §4.1) in the tokens-outermost
-[B][N][heads][d] layout of that section; K and V are then drawn with H_kv heads.
+[B][N][heads][d] layout of that section; K and V are then drawn with H_kv heads. A seventh is that
+layer decoding: one new query token per sequence (Nq = 1) against N = 32768 cached keys, for a
+batch of 8 sequences ("FlashAttention-2 -- Deeper Math", "What FA-2 does not fix"); Q is then drawn
+with Nq rows.
 """
 import math
 
@@ -33,6 +36,8 @@ WORKLOADS = {
                              sample_rows=64),
     "llama3_8b_gqa_n8k_causal": dict(B=1, H=32, H_kv=8, N=8192, d=128, dtype="bf16",
                                      causal=(True,), seed=5, layout="bnhd", sample_rows=64),
+    "llama3_8b_gqa_decode_b8_n32k": dict(B=8, H=32, H_kv=8, Nq=1, N=32768, d=128, dtype="bf16",
+                                         causal=(True,), seed=6, layout="bnhd"),
 }
 
 _TORCH_DTYPE = {"bf16": torch.bfloat16, "fp32": torch.float32}
@@ -62,12 +67,13 @@ def outlier_rows(N, count, seed):
 
 
 def make_inputs(B, H, N, d, dtype="bf16", seed=0, q_mult=1.0, outlier_frac=0.0,
-                outlier_mult=4.0, H_kv=None, **_ignored):
-    """Return (q, k, v) CPU tensors in the compute dtype: q [B, H, N, d], k and v [B, H_kv, N, d]
-    (H_kv defaults to H)."""
+                outlier_mult=4.0, H_kv=None, Nq=None, **_ignored):
+    """Return (q, k, v) CPU tensors in the compute dtype: q [B, H, Nq, d], k and v
+    [B, H_kv, N, d] (H_kv defaults to H, Nq to N)."""
     H_kv = H if H_kv is None else H_kv
+    Nq = N if Nq is None else Nq
     g = torch.Generator().manual_seed(seed)
-    q = torch.randn((B, H, N, d), generator=g, dtype=torch.float32)
+    q = torch.randn((B, H, Nq, d), generator=g, dtype=torch.float32)
     k = torch.randn((B, H_kv, N, d), generator=g, dtype=torch.float32)
     v = torch.randn((B, H_kv, N, d), generator=g, dtype=torch.float32)
     if q_mult != 1.0:

@@ -47,6 +47,8 @@
 #ifndef FA_H_
 #define FA_H_
 
+#include <stddef.h>
+
 #ifdef __cplusplus
 extern "C" {
 #endif
@@ -54,7 +56,7 @@ extern "C" {
 #define FA_OK 0
 #define FA_ERR_INVALID_ARG (-1) /* null pointer, B/H/N out of range, causal not 0/1, scale
                                    negative or not finite, or overlapping output buffers */
-#define FA_ERR_UNSUPPORTED (-2) /* head dim d not in {64, 128} */
+#define FA_ERR_UNSUPPORTED (-2) /* head dim d not in {64, 128}; split-KV: over 32 rows per K/V head */
 #define FA_ERR_ALIGNMENT (-3)   /* a pointer is not 16-byte aligned */
 #define FA_ERR_LAUNCH (-4)      /* the kernel launch call returned an error */
 
@@ -94,6 +96,37 @@ int fa_fwd_gqa(const void* q, const void* k, const void* v, void* o, float* lse,
 /* fa_fwd_gqa_f32 -- the fp32 counterpart of fa_fwd_gqa (as fa_fwd_f32 is of fa_fwd). */
 int fa_fwd_gqa_f32(const float* q, const float* k, const float* v, float* o, float* lse,
                    int B, int H, int H_kv, int N, int d, float scale, int causal, int layout,
+                   void* stream);
+
+/*
+ * Split-KV decoding ("FlashAttention-2 -- Deeper Math", "What FA-2 does not fix": few queries
+ * against a long K/V sequence are bound by reading K and V, so the keys are split across the GPU
+ * and the partial softmaxes merged with the blockwise recurrence of "Understanding FlashAttention
+ * Pt 1", §2.4). Shapes: q and o hold N_q query rows per head, k and v N_kv key rows per K/V head,
+ * in the given layout (FA_LAYOUT_BHND: q, o [B][H][N_q][d], k, v [B][H_kv][N_kv][d];
+ * FA_LAYOUT_BNHD: q, o [B][N_q][H][d], k, v [B][N_kv][H_kv][d]); lse [B][H][N_q]. Query head h uses
+ * K/V head h / (H / H_kv), as in fa_fwd_gqa. Query i is token N_kv - N_q + i of the sequence: with
+ * causal = 1 it sees keys j <= N_kv - N_q + i (then N_q <= N_kv is required), with causal = 0
+ * every key. The result is the same function fa_fwd_gqa computes for those masks; only the order
+ * of the floating-point operations differs.
+ *
+ * fa_splitkv_workspace_bytes -- bytes of device workspace fa_fwd_splitkv needs for this shape and
+ *   split count (n_splits = 0: the library's choice, about 768 waves of one (batch, K/V head,
+ *   split) each, at least 128 keys per split; a given count is capped at one split per 32 keys).
+ *   Returns 0 when the shape is not accepted by fa_fwd_splitkv.
+ * fa_fwd_splitkv -- bf16 q, k, v, o; fp32 arithmetic; fp32 partial results of every split in
+ *   `workspace` (caller-owned device memory of at least fa_splitkv_workspace_bytes(...) bytes,
+ *   16-byte aligned, overlapping nothing else; its contents on entry do not matter and are
+ *   overwritten). Two kernels are enqueued on `stream`; calls that share a workspace must not
+ *   overlap. Limits: N_kv <= 2^22, (H / H_kv) * N_q <= 32 (the query rows that share one K/V head
+ *   form one 32-row tile; more return FA_ERR_UNSUPPORTED), d in {64, 128}. Other conventions and
+ *   return codes as fa_fwd_gqa; a workspace that is NULL or too small returns FA_ERR_INVALID_ARG.
+ */
+size_t fa_splitkv_workspace_bytes(int B, int H, int H_kv, int N_q, int N_kv, int d, int causal,
+                                  int n_splits);
+int fa_fwd_splitkv(const void* q, const void* k, const void* v, void* o, float* lse,
+                   int B, int H, int H_kv, int N_q, int N_kv, int d, float scale, int causal,
+                   int layout, int n_splits, void* workspace, size_t workspace_bytes,
                    void* stream);
 
 /* Human-readable text for a return code (static storage; never NULL). */

@@ -8,7 +8,8 @@ Contents
 --------
 attention.py  -- the plain definition: materialise S = scale * Q K^T, mask, stable softmax,
                  O = P V and LSE = m + ln(l), in float64, one (batch, head) at a time; and the
-                 grouped-K/V-head form (each query head with its assigned K/V head).
+                 grouped-K/V-head form (each query head with its assigned K/V head), and the
+                 decoding form (N_q queries that are the last N_q of N_kv tokens).
 online.py     -- the pages' streaming recurrences (online normaliser, blockwise (m, l, a)
                  merge, tiled forward with queries outermost). A test model only: it is pinned
                  to attention.py, it is not what the GPU is compared against.
@@ -17,5 +18,6 @@ Every function is pinned by ``tests/test_oracle.py`` and ``tests/test_online_mod
 something other than itself: the worked example printed on the pages, closed forms,
 invariants, brute force in scalar Python, and float64 library routines.
 """
-from .attention import attention, attention_gqa, attention_head, dense_scores, kv_head_of  # noqa: F401
+from .attention import (attention, attention_decode, attention_gqa, attention_head,  # noqa: F401
+                        dense_scores, kv_head_of)
 from .online import online_normalizer, blockwise_row, tiled_attention  # noqa: F401

@@ -28,25 +28,29 @@ Readings where the pages leave a choice open:
 import numpy as np
 
 
-def dense_scores(q, k, scale, causal, rows):
+def dense_scores(q, k, scale, causal, rows, query_offset=0):
     """S = scale * q[rows] k^T with the causal rule applied (future keys -> -inf).
 
-    q: [Nq, d], k: [N, d] float64; rows: int array of query indices into q.
+    q: [Nq, d], k: [N, d] float64; rows: int array of query indices into q. Query row i is token
+    i + query_offset of the sequence (0 for self-attention over the same tokens), and the causal
+    rule keeps keys j <= i + query_offset.
     Returns S: [len(rows), N] float64.
     """
     s = float(scale) * (q[rows] @ k.T)
     if causal:
         key_pos = np.arange(k.shape[0])[None, :]
-        qry_pos = np.asarray(rows)[:, None]
+        qry_pos = np.asarray(rows)[:, None] + int(query_offset)
         s = np.where(key_pos <= qry_pos, s, -np.inf)
     return s
 
 
-def attention_head(q, k, v, scale, causal=False, rows=None, return_sp=False):
+def attention_head(q, k, v, scale, causal=False, rows=None, return_sp=False, query_offset=0):
     """One head of naive attention in float64.
 
-    q: [N, d], k: [N, d], v: [N, dv] (any float dtype; upcast to float64).
-    rows: optional sequence of query indices to evaluate (default: all N rows). Only those
+    q: [Nq, d], k: [N, d], v: [N, dv] (any float dtype; upcast to float64); Nq = N for
+       self-attention. query_offset: position of query row 0 in the key sequence (see
+       dense_scores).
+    rows: optional sequence of query indices to evaluate (default: all Nq rows). Only those
           rows of S are formed, each against every key.
     Returns (O [R, dv], LSE [R]) and, if return_sp, also (S [R, N], P [R, N]).
     """
@@ -56,7 +60,7 @@ def attention_head(q, k, v, scale, causal=False, rows=None, return_sp=False):
     if rows is None:
         rows = np.arange(q.shape[0])
     rows = np.asarray(rows, dtype=np.int64)
-    s = dense_scores(q, k, scale, causal, rows)
+    s = dense_scores(q, k, scale, causal, rows, query_offset)
     m = s.max(axis=1)
     if not np.all(np.isfinite(m)):
         raise ValueError("a query row has no visible key; its softmax is undefined")
@@ -132,4 +136,32 @@ def attention_gqa(q, k, v, scale, causal=False, rows=None):
                 ra = np.asarray(rows)
                 r = ra if ra.ndim == 1 else ra[b, h]
             o[b, h], lse[b, h] = attention_head(q[b, h], k[b, j], v[b, j], scale, causal, r)
+    return o, lse
+
+
+def attention_decode(q, k, v, scale, causal=False):
+    """Few queries against a longer key/value sequence, with grouped K/V heads, in float64.
+
+    q: [B, H, N_q, d]; k, v: [B, H_kv, N_kv, d] with N_q <= N_kv when causal. The queries are the
+    last N_q tokens of the N_kv-token sequence (query i is token N_kv - N_q + i), so with a causal
+    mask query i sees keys j <= N_kv - N_q + i and without one every key; query head h uses K/V
+    head kv_head_of(h, H, H_kv). This is the decoding problem of "FlashAttention-2 -- Deeper
+    Math" ("What FA-2 does not fix"), written out densely: the split over keys and the merge of
+    partial softmaxes are how the GPU reaches the same function.
+    Returns (O [B, H, N_q, dv], LSE [B, H, N_q]).
+    """
+    q = np.asarray(q)
+    k = np.asarray(k)
+    v = np.asarray(v)
+    B, H, Nq = q.shape[0], q.shape[1], q.shape[2]
+    H_kv, Nkv = k.shape[1], k.shape[2]
+    if causal and Nq > Nkv:
+        raise ValueError("with a causal mask the queries must be the last N_q of the N_kv tokens")
+    o = np.empty((B, H, Nq, v.shape[3]), dtype=np.float64)
+    lse = np.empty((B, H, Nq), dtype=np.float64)
+    for b in range(B):
+        for h in range(H):
+            j = kv_head_of(h, H, H_kv)
+            o[b, h], lse[b, h] = attention_head(q[b, h], k[b, j], v[b, j], scale, causal,
+                                                query_offset=Nkv - Nq)
     return o, lse

@@ -26,7 +26,8 @@ def _codes():
 
 
 def test_header_declares_the_expected_entry_points():
-    assert _declared() == ["fa_fwd", "fa_fwd_f32", "fa_fwd_gqa", "fa_fwd_gqa_f32", "fa_strerror",
+    assert _declared() == ["fa_fwd", "fa_fwd_f32", "fa_fwd_gqa", "fa_fwd_gqa_f32",
+                           "fa_fwd_splitkv", "fa_splitkv_workspace_bytes", "fa_strerror",
                            "fa_version"]
 
 
@@ -152,3 +153,57 @@ def test_forward_checks_gqa_shapes_before_any_gpu_use():
         fa.forward(q, k, torch.zeros(1, 2, 9, 64, dtype=torch.bfloat16))  # k, v differ
     with pytest.raises(ValueError):
         fa.forward(q, k, k)  # CPU tensors (shapes are fine)
+
+
+
+# ---- split-KV decoding ---------------------------------------------------------------------------
+W_ = A + 8 * (1 << 32)
+GOOD_DEC = dict(q=Q, k=K, v=V, o=O, lse=L, B=2, H=8, H_kv=2, Nq=1, Nkv=5000, d=128, scale=0.1,
+                causal=1, layout=0, n_splits=0, ws=W_, ws_bytes=1 << 30)
+
+
+def _call_dec(**kw):
+    a = dict(GOOD_DEC, **kw)
+    return fa.fa_fwd_splitkv(a["q"], a["k"], a["v"], a["o"], a["lse"], a["B"], a["H"], a["H_kv"],
+                             a["Nq"], a["Nkv"], a["d"], a["scale"], a["causal"], a["layout"],
+                             a["n_splits"], a["ws"], a["ws_bytes"], None)
+
+
+BAD_DEC = [
+    (dict(ws=0), fa.FA_ERR_INVALID_ARG),
+    (dict(ws_bytes=16), fa.FA_ERR_INVALID_ARG),           # too small
+    (dict(q=0), fa.FA_ERR_INVALID_ARG),
+    (dict(Nq=0), fa.FA_ERR_INVALID_ARG),
+    (dict(Nkv=0), fa.FA_ERR_INVALID_ARG),
+    (dict(Nkv=(1 << 22) + 1), fa.FA_ERR_INVALID_ARG),
+    (dict(Nq=6000), fa.FA_ERR_INVALID_ARG),               # causal needs N_q <= N_kv
+    (dict(H_kv=3), fa.FA_ERR_INVALID_ARG),
+    (dict(layout=5), fa.FA_ERR_INVALID_ARG),
+    (dict(causal=2), fa.FA_ERR_INVALID_ARG),
+    (dict(scale=float("nan")), fa.FA_ERR_INVALID_ARG),
+    (dict(n_splits=-1), fa.FA_ERR_INVALID_ARG),
+    (dict(Nq=9), fa.FA_ERR_UNSUPPORTED),                  # 4 heads x 9 queries > 32 rows
+    (dict(H=64, H_kv=1), fa.FA_ERR_UNSUPPORTED),         # 64 heads share one K/V head
+    (dict(d=96), fa.FA_ERR_UNSUPPORTED),
+    (dict(ws=W_ + 8), fa.FA_ERR_ALIGNMENT),
+    (dict(ws=Q), fa.FA_ERR_INVALID_ARG),                  # workspace overlaps q
+    (dict(o=K), fa.FA_ERR_INVALID_ARG),                   # o overlaps k
+]
+
+
+@pytest.mark.parametrize("kw,code", BAD_DEC, ids=[str(b[0]) for b in BAD_DEC])
+def test_bad_splitkv_arguments_are_refused(kw, code):
+    assert _call_dec(**kw) == code
+
+
+def test_splitkv_workspace_bytes():
+    f = fa.fa_splitkv_workspace_bytes
+    # B * H_kv * splits * R * (d + 1) floats, the LSE part starting on a 256-byte boundary
+    n = f(1, 8, 2, 1, 4096, 128, 1, 16)
+    R, splits = 4, 16
+    o_part = 2 * splits * R * 128 * 4
+    assert n == (o_part + 255) // 256 * 256 + 2 * splits * R * 4
+    assert f(1, 8, 2, 1, 4096, 128, 1, 0) > 0          # library's own split count
+    assert f(1, 8, 2, 9, 4096, 128, 1, 0) == 0          # 36 rows per K/V head: not accepted
+    assert f(1, 8, 3, 1, 4096, 128, 1, 0) == 0          # uneven head groups
+    assert f(1, 8, 2, 1, 40, 128, 1, 1000) == f(1, 8, 2, 1, 40, 128, 1, 2)  # at most 1 split / 32 keys
