@@ -10,14 +10,17 @@ attention.py  -- the plain definition: materialise S = scale * Q K^T, mask, stab
                  O = P V and LSE = m + ln(l), in float64, one (batch, head) at a time; and the
                  grouped-K/V-head form (each query head with its assigned K/V head), and the
                  decoding form (N_q queries that are the last N_q of N_kv tokens).
+backward.py   -- the gradients of the plain definition (dQ, dK, dV from dO), dense, in float64,
+                 per head and with grouped K/V heads.
 online.py     -- the pages' streaming recurrences (online normaliser, blockwise (m, l, a)
                  merge, tiled forward with queries outermost). A test model only: it is pinned
                  to attention.py, it is not what the GPU is compared against.
 
-Every function is pinned by ``tests/test_oracle.py`` and ``tests/test_online_model.py`` to
+Every function is pinned by ``tests/test_oracle*.py`` and ``tests/test_online_model.py`` to
 something other than itself: the worked example printed on the pages, closed forms,
 invariants, brute force in scalar Python, and float64 library routines.
 """
 from .attention import (attention, attention_decode, attention_gqa, attention_head,  # noqa: F401
                         dense_scores, kv_head_of)
+from .backward import attention_backward, attention_backward_head  # noqa: F401
 from .online import online_normalizer, blockwise_row, tiled_attention  # noqa: F401
