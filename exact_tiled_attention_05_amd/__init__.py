@@ -1,8 +1,8 @@
-"""Exact tiled attention forward pass for AMD MI355X (gfx950): Python binding of ``libfa.so``.
+"""Exact tiled attention for AMD MI355X (gfx950): Python binding of ``libfa.so``.
 
 The library computes, per batch and head, O = softmax(scale * Q K^T [causal mask]) V and the
-per-row logsumexp, tile by tile, without ever writing the N x N score matrix (see
-``include/fa.h`` for the full contract). This module only marshals arguments: every step of the
+per-row logsumexp, tile by tile, without ever writing the N x N score matrix, and the gradients
+dQ, dK, dV by recomputing those tiles (see ``include/fa.h`` for the full contract). This module only marshals arguments: every step of the
 computation runs in the HIP kernels of ``libfa.so``. There is no CPU fallback; if the library
 is missing the calls raise.
 
@@ -14,6 +14,9 @@ Raw entry points (same names and argument order as the C-ABI; pointers are integ
     fa_splitkv_workspace_bytes(B, H, H_kv, N_q, N_kv, d, causal, n_splits) -> int
     fa_fwd_splitkv(q, k, v, o, lse, B, H, H_kv, N_q, N_kv, d, scale, causal, layout, n_splits,
                    workspace, workspace_bytes, stream) -> int
+    fa_bwd_workspace_bytes(B, H, N) -> int
+    fa_bwd(q, k, v, o, dout, lse, dq, dk, dv, B, H, H_kv, N, d, scale, causal, layout, workspace,
+           workspace_bytes, stream) -> int
     fa_strerror(code) -> str
     fa_version() -> int
 Tensor convenience (PyTorch supplies device memory and the stream):
@@ -21,12 +24,15 @@ Tensor convenience (PyTorch supplies device memory and the stream):
         -> (o, lse)
     decode(q, k, v, scale=None, causal=False, layout="bhnd", n_splits=0, out=None, lse=None,
            workspace=None, stream=None) -> (o, lse)
+    backward(q, k, v, o, lse, dout, scale=None, causal=False, layout="bhnd", dq=None, dk=None,
+             dv=None, workspace=None, stream=None) -> (dq, dk, dv)
 """
 import ctypes
 import math
 import os
 
-__all__ = ["fa_fwd", "fa_fwd_f32", "fa_fwd_gqa", "fa_fwd_gqa_f32", "fa_fwd_splitkv",
+__all__ = ["fa_fwd", "fa_fwd_f32", "fa_fwd_gqa", "fa_fwd_gqa_f32", "fa_fwd_splitkv", "fa_bwd",
+           "fa_bwd_workspace_bytes", "backward",
            "fa_splitkv_workspace_bytes", "fa_strerror", "fa_version", "forward", "decode", "FAError", "library_path", "load_library", "FA_OK", "FA_ERR_INVALID_ARG",
            "FA_ERR_UNSUPPORTED", "FA_ERR_ALIGNMENT", "FA_ERR_LAUNCH", "FA_LAYOUT_BHND",
            "FA_LAYOUT_BNHD"]
@@ -77,6 +83,12 @@ def load_library():
                                        [ctypes.c_float] + [ctypes.c_int] * 3 +
                                        [ctypes.c_void_p, ctypes.c_size_t, ctypes.c_void_p])
         lib.fa_fwd_splitkv.restype = ctypes.c_int
+        lib.fa_bwd_workspace_bytes.argtypes = [ctypes.c_int] * 3
+        lib.fa_bwd_workspace_bytes.restype = ctypes.c_size_t
+        lib.fa_bwd.argtypes = ([ctypes.c_void_p] * 9 + [ctypes.c_int] * 5 + [ctypes.c_float] +
+                               [ctypes.c_int] * 2 + [ctypes.c_void_p, ctypes.c_size_t,
+                                                     ctypes.c_void_p])
+        lib.fa_bwd.restype = ctypes.c_int
         lib.fa_strerror.argtypes = [ctypes.c_int]
         lib.fa_strerror.restype = ctypes.c_char_p
         lib.fa_version.argtypes = []
@@ -111,6 +123,16 @@ def fa_fwd_splitkv(q, k, v, o, lse, B, H, H_kv, N_q, N_kv, d, scale, causal, lay
                    workspace, workspace_bytes, stream=None):
     return load_library().fa_fwd_splitkv(q, k, v, o, lse, B, H, H_kv, N_q, N_kv, d, scale, causal,
                                          layout, n_splits, workspace, workspace_bytes, stream)
+
+
+def fa_bwd_workspace_bytes(B, H, N):
+    return load_library().fa_bwd_workspace_bytes(B, H, N)
+
+
+def fa_bwd(q, k, v, o, dout, lse, dq, dk, dv, B, H, H_kv, N, d, scale, causal, layout, workspace,
+           workspace_bytes, stream=None):
+    return load_library().fa_bwd(q, k, v, o, dout, lse, dq, dk, dv, B, H, H_kv, N, d, scale,
+                                 causal, layout, workspace, workspace_bytes, stream)
 
 
 def fa_strerror(code):
@@ -228,3 +250,56 @@ def decode(q, k, v, scale=None, causal=False, layout="bhnd", n_splits=0, out=Non
     if rc != FA_OK:
         raise FAError(rc, "fa_fwd_splitkv")
     return out, lse
+
+
+def backward(q, k, v, o, lse, dout, scale=None, causal=False, layout="bhnd", dq=None, dk=None,
+             dv=None, workspace=None, stream=None):
+    """Gradients of attention (bf16 CUDA/HIP tensors, contiguous) by recomputation.
+
+    q, o, dout like forward()'s q and o; k, v its k and v; lse the float32 [B, H, N] logsumexp
+    forward() returned for the same q, k, v, scale and mask. Returns (dq, dk, dv) shaped like q, k,
+    v; for grouped K/V heads dk and dv hold the sums over each K/V head's query heads.
+    ``workspace`` (a uint8 tensor of at least fa_bwd_workspace_bytes(B, H, N) bytes) is allocated
+    here if not given.
+    """
+    import torch
+
+    if layout not in ("bhnd", "bnhd"):
+        raise ValueError("layout must be 'bhnd' or 'bnhd'")
+    if q.dim() != 4 or k.dim() != 4 or k.shape != v.shape or o.shape != q.shape or \
+            dout.shape != q.shape:
+        raise ValueError("q, o, dout must share a shape and k, v must share a shape (4-D)")
+    if layout == "bhnd":
+        B, H, N, d = q.shape
+        Bk, H_kv, Nk, dk_ = k.shape
+    else:
+        B, N, H, d = q.shape
+        Bk, Nk, H_kv, dk_ = k.shape
+    if (Bk, Nk, dk_) != (B, N, d) or H_kv < 1 or H % H_kv != 0:
+        raise ValueError("k, v must match q in batch, length and head dim, with H a multiple of "
+                         "their head count")
+    if not all(t.dtype == torch.bfloat16 for t in (q, k, v, o, dout)):
+        raise ValueError("q, k, v, o, dout must all be bfloat16")
+    if lse.dtype != torch.float32 or tuple(lse.shape) != (B, H, N):
+        raise ValueError("lse must be float32 [B, H, N]")
+    ts = (q, k, v, o, dout, lse)
+    if not all(t.is_cuda and t.device == q.device and t.is_contiguous() for t in ts):
+        raise ValueError("all tensors must be contiguous and on the same GPU device")
+    if scale is None:
+        scale = 1.0 / math.sqrt(d)
+    dq = torch.empty_like(q) if dq is None else dq
+    dk = torch.empty_like(k) if dk is None else dk
+    dv = torch.empty_like(v) if dv is None else dv
+    need = fa_bwd_workspace_bytes(B, H, N)
+    if workspace is None:
+        workspace = torch.empty(max(need, 1), dtype=torch.uint8, device=q.device)
+    if stream is None:
+        stream = torch.cuda.current_stream(q.device).cuda_stream
+    lay = FA_LAYOUT_BHND if layout == "bhnd" else FA_LAYOUT_BNHD
+    rc = fa_bwd(q.data_ptr(), k.data_ptr(), v.data_ptr(), o.data_ptr(), dout.data_ptr(),
+                lse.data_ptr(), dq.data_ptr(), dk.data_ptr(), dv.data_ptr(), B, H, H_kv, N, d,
+                float(scale), int(bool(causal)), lay, workspace.data_ptr(),
+                workspace.numel() * workspace.element_size(), stream)
+    if rc != FA_OK:
+        raise FAError(rc, "fa_bwd")
+    return dq, dk, dv

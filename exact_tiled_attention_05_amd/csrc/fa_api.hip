@@ -8,13 +8,14 @@
 #include <cstdint>
 
 #include "fa.h"
+#include "fa_bwd.h"
 #include "fa_decode.h"
 #include "fa_fwd_bf16.h"
 #include "fa_fwd_f32.h"
 
 namespace {
 
-constexpr int kVersion = 300;  // 0.3.0: split-KV decoding
+constexpr int kVersion = 400;  // 0.4.0: backward pass
 constexpr int kMaxN = 1 << 22;
 constexpr int kMaxBH = 65535;  // grid y of the fp32 kernel; also keeps bf16 grids < 2^31
 
@@ -185,9 +186,91 @@ hipError_t launch_decode(fa::DecodeArgs a, hipStream_t s) {
                          dim3(a.R, a.B_Hkv()), dim3(fa::kCombineThreads), args, 0, s);
 }
 
+// ---- backward ----------------------------------------------------------------------------------
+
+size_t bwd_ws_bytes(int B, int H, int N) { return (size_t)B * H * N * sizeof(float); }
+
+template <int D, bool CAUSAL>
+hipError_t launch_bwd(fa::BwdArgs a, hipStream_t s) {
+  void* args[] = {&a};
+  hipError_t e = hipLaunchKernel(reinterpret_cast<const void*>(&fa::fa_bwd_dq_kernel<D, CAUSAL>),
+                                 dim3(a.n_qblk * a.BH), dim3(fa::kBwdWaves * 64), args, 0, s);
+  if (e != hipSuccess) return e;
+  return hipLaunchKernel(reinterpret_cast<const void*>(&fa::fa_bwd_dkdv_kernel<D, CAUSAL>),
+                         dim3(a.n_kblk * a.BHkv), dim3(fa::kBwdWaves * 64), args, 0, s);
+}
+
 }  // namespace
 
 extern "C" {
+
+size_t fa_bwd_workspace_bytes(int B, int H, int N) {
+  if (B < 1 || H < 1 || N < 1 || N > kMaxN || (int64_t)B * H > kMaxBH) return 0;
+  return bwd_ws_bytes(B, H, N);
+}
+
+int fa_bwd(const void* q, const void* k, const void* v, const void* o, const void* dout,
+           const float* lse, void* dq, void* dk, void* dv, int B, int H, int H_kv, int N, int d,
+           float scale, int causal, int layout, void* workspace, size_t workspace_bytes,
+           void* stream) {
+  if (!dout || !dq || !dk || !dv || !workspace) return FA_ERR_INVALID_ARG;
+  int rc = check_args(q, k, v, o, lse, B, H, H_kv, N, d, scale, causal, layout, 2);
+  if (rc != FA_OK) return rc;
+  const uintptr_t mis = reinterpret_cast<uintptr_t>(dout) | reinterpret_cast<uintptr_t>(dq) |
+                        reinterpret_cast<uintptr_t>(dk) | reinterpret_cast<uintptr_t>(dv) |
+                        reinterpret_cast<uintptr_t>(workspace);
+  if (mis & 15) return FA_ERR_ALIGNMENT;
+  const size_t wb = bwd_ws_bytes(B, H, N);
+  if (workspace_bytes < wb) return FA_ERR_INVALID_ARG;
+  const size_t qb = (size_t)B * H * N * d * 2, kb = (size_t)B * H_kv * N * d * 2;
+  const size_t lb = (size_t)B * H * N * sizeof(float);
+  const void* ins[6] = {q, k, v, o, dout, lse};
+  const size_t insz[6] = {qb, kb, kb, qb, qb, lb};
+  const void* outs[4] = {dq, dk, dv, workspace};
+  const size_t outsz[4] = {qb, kb, kb, wb};
+  for (int i = 0; i < 4; i++) {
+    for (int j = 0; j < 6; j++)
+      if (ranges_overlap(outs[i], outsz[i], ins[j], insz[j])) return FA_ERR_INVALID_ARG;
+    for (int j = i + 1; j < 4; j++)
+      if (ranges_overlap(outs[i], outsz[i], outs[j], outsz[j])) return FA_ERR_INVALID_ARG;
+  }
+
+  fa::BwdArgs a;
+  a.q = static_cast<const fa::bf16*>(q);
+  a.k = static_cast<const fa::bf16*>(k);
+  a.v = static_cast<const fa::bf16*>(v);
+  a.o = static_cast<const fa::bf16*>(o);
+  a.dout = static_cast<const fa::bf16*>(dout);
+  a.lse = lse;
+  a.dq = static_cast<fa::bf16*>(dq);
+  a.dk = static_cast<fa::bf16*>(dk);
+  a.dv = static_cast<fa::bf16*>(dv);
+  a.dsum = static_cast<float*>(workspace);
+  a.N = N;
+  a.H = H;
+  a.Hkv = H_kv;
+  a.group = H / H_kv;
+  a.BH = B * H;
+  a.BHkv = B * H_kv;
+  a.n_qblk = (N + fa::kBwdRows - 1) / fa::kBwdRows;
+  a.n_kblk = a.n_qblk;
+  a.scale = scale;
+  a.scale_log2 = scale * fa::kLog2e;
+  const Strides sq = strides_of(layout, H, N, d), sk = strides_of(layout, H_kv, N, d);
+  a.q_bs = sq.bs;
+  a.q_hs = sq.hs;
+  a.q_rs = sq.rs;
+  a.kv_bs = sk.bs;
+  a.kv_hs = sk.hs;
+  a.kv_rs = sk.rs;
+  const hipStream_t s = static_cast<hipStream_t>(stream);
+  hipError_t e;
+  if (d == 128)
+    e = causal ? launch_bwd<128, true>(a, s) : launch_bwd<128, false>(a, s);
+  else
+    e = causal ? launch_bwd<64, true>(a, s) : launch_bwd<64, false>(a, s);
+  return e == hipSuccess ? FA_OK : FA_ERR_LAUNCH;
+}
 
 size_t fa_splitkv_workspace_bytes(int B, int H, int H_kv, int N_q, int N_kv, int d, int causal,
                                   int n_splits) {

@@ -1,0 +1,380 @@
+// Attention backward by recomputation, bf16 in / bf16 out, fp32 arithmetic, gfx950.
+//
+// "Understanding FlashAttention Pt 1", §3.6: the forward pass keeps O and one statistic per row;
+// the backward pass rebuilds each tile of P from Q K^T and that statistic -- the logsumexp L of
+// "FlashAttention-2 -- Deeper Math", Fix 2, so P_ij = exp(scale q_i.k_j - L_i) -- and forms, per
+// tile,
+//     dV += P^T dO,   dP = dO V^T,   dS = P * (dP - D),   dQ += scale dS K,   dK += scale dS^T Q,
+// with D_i = sum_r dO_ir O_ir (the row identity of the same section) and masked entries
+// contributing nothing. Nothing of size N x N is stored.
+//
+// Two kernels, so that every output element is summed by exactly one wave in a fixed order (no
+// atomics, bit-reproducible):
+//   fa_bwd_dq_kernel (queries outermost, like the forward): 4 waves x 32 query rows per
+//     workgroup. A wave keeps its rows' Q^T and dO^T operands in registers and computes D for them
+//     first (and stores it for the second kernel); per 32-key step of the K/V tiles in LDS:
+//     S^T = K Q^T, dP^T = V dO^T (keys on M, queries on N, as in the forward kernel), P^T and dS^T
+//     in fp32, then dQ^T += K^T dS^T with dS^T rounded to bf16 as the B operand and K^T read
+//     with the transposing LDS read.
+//   fa_bwd_dkdv_kernel (keys outermost): 4 waves x 32 keys per workgroup. A wave keeps its keys'
+//     K and V rows in registers as B operands and loops over the query tiles -- of every query
+//     head that shares the K/V head, so grouped heads receive the sum of their query heads'
+//     gradients -- with Q, dO, L and D of each 64-query tile in LDS: S = Q K^T, dP = dO V^T
+//     (queries on M, keys on N), P and dS in fp32, then dV^T += dO^T P and dK^T += Q^T dS with
+//     P, dS rounded to bf16 and dO^T, Q^T read with the transposing LDS read.
+//
+// LDS layout of a 64-row tile: unpadded rows of 2d bytes; the 16-byte chunk j of row r is stored
+// at chunk position j ^ f(r). Tiles here are read both ways -- as rows (16 bytes of one row per
+// lane, 16 consecutive rows per group of lanes) and transposed (ds_read_b64_tr_b16: 8 bytes from
+// each of 8 rows x 64 bytes) -- and no padding serves both; the swizzle f below is chosen so that
+// both reads, and the staging writes, touch every bank equally often.
+#pragma once
+
+#include "fa_device.h"
+
+namespace fa {
+
+constexpr int kBwdWaves = 4;
+constexpr int kBwdRows = 32 * kBwdWaves;  // query rows (dQ kernel) or keys (dK/dV kernel) per workgroup
+constexpr int kBwdTile = 64;              // rows of a K/V tile (dQ kernel) or a Q/dO tile (dK/dV kernel)
+
+typedef unsigned int u32x4v __attribute__((ext_vector_type(4)));
+typedef float f32x4v __attribute__((ext_vector_type(4)));
+
+struct BwdArgs {
+  const bf16* q;
+  const bf16* k;
+  const bf16* v;
+  const bf16* o;
+  const bf16* dout;
+  const float* lse;
+  bf16* dq;
+  bf16* dk;
+  bf16* dv;
+  float* dsum;  // D, [B * H][N] fp32 (written by the dQ kernel, read by the dK/dV kernel)
+  int N, H, Hkv, group;
+  int BH, BHkv;  // B * H, B * H_kv
+  int n_qblk, n_kblk;
+  float scale, scale_log2;
+  long long q_bs, q_hs, kv_bs, kv_hs;  // element strides of batch and head (q, o, dO, dQ share q's)
+  int q_rs, kv_rs;                     // element stride between consecutive rows of one head
+};
+
+// Swizzled tile geometry for head dim D (see the header comment).
+template <int D>
+struct Swz {
+  static constexpr int ROW = 2 * D;  // bytes per row
+  static constexpr int CPR = D / 8;  // 16-byte chunks per row
+  static constexpr int BYTES = kBwdTile * ROW;
+  // d = 128 (16 chunks): row reads need f injective on 16 consecutive rows; the transposing read
+  // of rows 8u..8u+7 x chunks 4b..4b+3 needs (chunk ^ f) to hit each of the 16 positions twice:
+  // f(r) = 2 (r mod 8) + bit 3 of r does both. d = 64 (8 chunks, two rows per 256 bytes): f is a
+  // bit permutation of r / 2 that puts bits 1 and 2 of r on chunk bits 0 and 2.
+  __device__ static __forceinline__ int f(int r) {
+    if constexpr (D == 128) return ((r & 7) << 1) | ((r >> 3) & 1);
+    else return ((r >> 1) & 1) | (((r >> 3) & 1) << 1) | (((r >> 2) & 1) << 2);
+  }
+  __device__ static __forceinline__ int off(int r, int j) { return r * ROW + 16 * (j ^ f(r)); }
+};
+
+// One 64-row tile staged in registers: 256 threads, each one 16-byte chunk per piece.
+template <int D>
+struct BwdStage {
+  static constexpr int PIECES = kBwdTile * Swz<D>::CPR / 256;
+  static constexpr int RPP = 256 / Swz<D>::CPR;  // rows per piece
+  u32x4v r[PIECES];
+};
+
+// Rows row0 .. row0+63 of one head (rows at byte stride rs) into registers; rows at or past N read
+// as zeros (the buffer resource ends at row N-1).
+template <int D>
+__device__ __forceinline__ void bwd_load(const char* head, long long rs, int row0, int N, int tid,
+                                         BwdStage<D>& st) {
+  constexpr int CPR = Swz<D>::CPR;
+  const int rows = min(N - row0, kBwdTile);  // >= 1: only tiles that start below N are loaded
+  const __amdgpu_buffer_rsrc_t r = __builtin_amdgcn_make_buffer_rsrc(
+      (void*)(head + (long long)row0 * rs), 0, (int)((rows - 1) * rs) + 2 * D, 0x00020000);
+  const int voff = (int)((tid / CPR) * rs) + 16 * (tid % CPR);
+#pragma unroll
+  for (int i = 0; i < BwdStage<D>::PIECES; i++)
+    st.r[i] = __builtin_bit_cast(
+        u32x4v, __builtin_amdgcn_raw_buffer_load_b128(r, voff, (int)(i * BwdStage<D>::RPP * rs), 0));
+}
+
+template <int D>
+__device__ __forceinline__ void bwd_store(char* tile, int tid, const BwdStage<D>& st) {
+  constexpr int CPR = Swz<D>::CPR;
+#pragma unroll
+  for (int i = 0; i < BwdStage<D>::PIECES; i++) {
+    const int slot = i * 256 + tid;
+    *(FA_LDS u32x4v*)(tile + Swz<D>::off(slot / CPR, slot % CPR)) = st.r[i];
+  }
+}
+
+// Row operand: 8 consecutive elements (chunk 2 dk + h) of tile row r.
+template <int D>
+__device__ __forceinline__ bf16x8 bwd_row(const char* tile, int r, int dk, int h) {
+  return lds_read_b128(tile + Swz<D>::off(r, 2 * dk + h));
+}
+
+// Transposed operand of one 16-row k-step: for lane (c, h) the 8 values of column 32 db + c from
+// rows r0 + {4h..4h+3, 8+4h..8+4h+3}, the row order of one k-step of the 32x32 accumulator.
+template <int D>
+__device__ __forceinline__ bf16x8 bwd_tr(const char* tile, int r0, int db, int lane) {
+  const int Lg = lane & 15, h = lane >> 5, hi = (lane >> 4) & 1;
+  const int col = 64 * db + 32 * hi + 8 * (Lg & 3);  // byte column
+  const int ra = r0 + 4 * h + (Lg >> 2), rb = ra + 8;
+  const bf16x4 x = lds_read_tr16(tile + Swz<D>::off(ra, col >> 4) + (col & 15));
+  const bf16x4 y = lds_read_tr16(tile + Swz<D>::off(rb, col >> 4) + (col & 15));
+  return __builtin_shufflevector(x, y, 0, 1, 2, 3, 4, 5, 6, 7);
+}
+
+// Row index (within a 32-row step) of accumulator register i of lane half h.
+__device__ __forceinline__ constexpr int acc_row(int i, int h) { return 8 * (i >> 2) + 4 * h + (i & 3); }
+
+// ---------------------------------------------------------------------------------------------
+// dQ (and D)
+// ---------------------------------------------------------------------------------------------
+template <int D, bool CAUSAL>
+__global__ __launch_bounds__(256) __attribute__((amdgpu_waves_per_eu(2))) void fa_bwd_dq_kernel(BwdArgs a) {
+  constexpr int DK = D / 16, DB = D / 32;
+  using S = Swz<D>;
+  __shared__ __attribute__((aligned(1024))) char sK[S::BYTES];
+  __shared__ __attribute__((aligned(1024))) char sV[S::BYTES];
+
+  const int tid = threadIdx.x, wave = tid >> 6, lane = tid & 63;
+  const int c = lane & 31, h = lane >> 5;
+  int bh, qblk;
+  map_block<CAUSAL>(blockIdx.x, gridDim.x, a.BH, a.n_qblk, bh, qblk);
+  const int b = bh / a.H, hq = bh - b * a.H, hk = hq / a.group;
+  const int N = a.N;
+  const int qw0 = qblk * kBwdRows + 32 * wave;
+  const int qrow = qw0 + c;
+  const long long qoff = b * a.q_bs + hq * a.q_hs + (long long)qrow * a.q_rs;
+  const long long kvhead = b * a.kv_bs + hk * a.kv_hs;
+  const long long rs = 2LL * a.kv_rs;
+
+  // Q^T and dO^T operands of this lane's row; D = sum_r dO_r O_r over the row (two lanes hold
+  // halves of it).
+  bf16x8 qf[DK], df[DK];
+  float dpart = 0.f;
+#pragma unroll
+  for (int dk = 0; dk < DK; dk++) {
+    if (qrow < N) {
+      qf[dk] = *reinterpret_cast<const bf16x8*>(a.q + qoff + dk * 16 + h * 8);
+      df[dk] = *reinterpret_cast<const bf16x8*>(a.dout + qoff + dk * 16 + h * 8);
+      const bf16x8 ov = *reinterpret_cast<const bf16x8*>(a.o + qoff + dk * 16 + h * 8);
+#pragma unroll
+      for (int e = 0; e < 8; e++) dpart = __builtin_fmaf((float)df[dk][e], (float)ov[e], dpart);
+    } else {
+      qf[dk] = bf16x8{};
+      df[dk] = bf16x8{};
+    }
+  }
+  const float drow = half_swap_sum(dpart);
+  float lse2 = 0.f;
+  if (qrow < N) {
+    if (h == 0) a.dsum[(long long)bh * N + qrow] = drow;
+    lse2 = a.lse[(long long)bh * N + qrow] * kLog2e;
+  }
+
+  f32x16 acc[DB];
+#pragma unroll
+  for (int db = 0; db < DB; db++) acc[db] = f32x16{};
+
+  const int wave_last = CAUSAL ? min(N - 1, qw0 + 31) : N - 1;  // last key this wave needs
+  const int blk_last = CAUSAL ? min(N - 1, qblk * kBwdRows + kBwdRows - 1) : N - 1;
+  const int n_kt = blk_last / kBwdTile + 1;
+  const char* kh = reinterpret_cast<const char*>(a.k + kvhead);
+  const char* vh = reinterpret_cast<const char*>(a.v + kvhead);
+  BwdStage<D> stk, stv;
+  bwd_load<D>(kh, rs, 0, N, tid, stk);
+  bwd_load<D>(vh, rs, 0, N, tid, stv);
+
+  for (int j = 0; j < n_kt; j++) {
+    if (j > 0) __syncthreads();  // every wave is done with tile j-1
+    bwd_store<D>(sK, tid, stk);
+    bwd_store<D>(sV, tid, stv);
+    __syncthreads();
+    if (j + 1 < n_kt) {
+      bwd_load<D>(kh, rs, (j + 1) * kBwdTile, N, tid, stk);
+      bwd_load<D>(vh, rs, (j + 1) * kBwdTile, N, tid, stv);
+    }
+#pragma unroll
+    for (int sb = 0; sb < 2; sb++) {
+      const int k0 = j * kBwdTile + 32 * sb;
+      if (k0 > wave_last) continue;
+      f32x16 st = f32x16{}, dpt = f32x16{};
+#pragma unroll
+      for (int dk = 0; dk < DK; dk++)
+        st = __builtin_amdgcn_mfma_f32_32x32x16_bf16(bwd_row<D>(sK, 32 * sb + c, dk, h), qf[dk], st, 0, 0, 0);
+#pragma unroll
+      for (int dk = 0; dk < DK; dk++)
+        dpt = __builtin_amdgcn_mfma_f32_32x32x16_bf16(bwd_row<D>(sV, 32 * sb + c, dk, h), df[dk], dpt, 0, 0, 0);
+      // P^T = exp(S^T scale - L), masked; dS^T = P^T (dP^T - D)
+      const bool edge = (CAUSAL && k0 + 31 > qw0) || k0 + 31 >= N;
+      bf16x8 dsf[2];
+#pragma unroll
+      for (int i = 0; i < 16; i++) {
+        float p = fast_exp2(__builtin_fmaf(st[i], a.scale_log2, -lse2));
+        if (edge) {
+          const int key = k0 + acc_row(i, h);
+          if (key >= N || (CAUSAL && key > qrow)) p = 0.f;
+        }
+        dsf[i >> 3][i & 7] = (bf16)(p * (dpt[i] - drow));
+      }
+#pragma unroll
+      for (int ks = 0; ks < 2; ks++)
+#pragma unroll
+        for (int db = 0; db < DB; db++)
+          acc[db] = __builtin_amdgcn_mfma_f32_32x32x16_bf16(bwd_tr<D>(sK, 32 * sb + 16 * ks, db, lane),
+                                                            dsf[ks], acc[db], 0, 0, 0);
+    }
+  }
+
+  if (qrow < N) {
+    bf16* dst = a.dq + qoff;
+#pragma unroll
+    for (int db = 0; db < DB; db++)
+#pragma unroll
+      for (int g4 = 0; g4 < 4; g4++) {
+        bf16x4 v4;
+#pragma unroll
+        for (int e = 0; e < 4; e++) v4[e] = (bf16)(acc[db][4 * g4 + e] * a.scale);
+        *reinterpret_cast<bf16x4*>(dst + 32 * db + 8 * g4 + 4 * h) = v4;
+      }
+  }
+}
+
+// ---------------------------------------------------------------------------------------------
+// dK, dV
+// ---------------------------------------------------------------------------------------------
+template <int D, bool CAUSAL>
+__global__ __launch_bounds__(256) __attribute__((amdgpu_waves_per_eu(1, 1))) void fa_bwd_dkdv_kernel(BwdArgs a) {
+  constexpr int DK = D / 16, DB = D / 32;
+  using S = Swz<D>;
+  __shared__ __attribute__((aligned(1024))) char sQ[S::BYTES];
+  __shared__ __attribute__((aligned(1024))) char sO[S::BYTES];  // dO
+  __shared__ __attribute__((aligned(16))) float sL[kBwdTile];    // L * log2(e)
+  __shared__ __attribute__((aligned(16))) float sD[kBwdTile];    // D
+
+  const int tid = threadIdx.x, wave = tid >> 6, lane = tid & 63;
+  const int c = lane & 31, h = lane >> 5;
+  int bkv, x;
+  map_block<CAUSAL>(blockIdx.x, gridDim.x, a.BHkv, a.n_kblk, bkv, x);
+  const int kblk = CAUSAL ? a.n_kblk - 1 - x : x;  // causal: the first key blocks, which see the
+                                                   // most queries, first
+  const int b = bkv / a.Hkv, hk = bkv - b * a.Hkv;
+  const int N = a.N;
+  const int kw0 = kblk * kBwdRows + 32 * wave;
+  const int krow = kw0 + c;
+  const long long kvoff = b * a.kv_bs + hk * a.kv_hs + (long long)krow * a.kv_rs;
+  const long long rs = 2LL * a.q_rs;
+
+  bf16x8 kf[DK], vf[DK];
+#pragma unroll
+  for (int dk = 0; dk < DK; dk++) {
+    kf[dk] = krow < N ? *reinterpret_cast<const bf16x8*>(a.k + kvoff + dk * 16 + h * 8) : bf16x8{};
+    vf[dk] = krow < N ? *reinterpret_cast<const bf16x8*>(a.v + kvoff + dk * 16 + h * 8) : bf16x8{};
+  }
+  f32x16 acck[DB], accv[DB];
+#pragma unroll
+  for (int db = 0; db < DB; db++) {
+    acck[db] = f32x16{};
+    accv[db] = f32x16{};
+  }
+
+  const int t0 = CAUSAL ? (kblk * kBwdRows) / kBwdTile : 0;  // first query tile with a visible key
+  const int n_qt = (N + kBwdTile - 1) / kBwdTile;
+  const int n_steps = a.group * (n_qt - t0);  // (query head, query tile) pairs, in that order
+  BwdStage<D> stq, sto;
+  float lsd = 0.f;
+  auto load_step = [&](int s) {
+    const int g = s / (n_qt - t0), t = t0 + s % (n_qt - t0);
+    const int bh = b * a.H + hk * a.group + g;
+    const long long qhead = b * a.q_bs + (long long)(hk * a.group + g) * a.q_hs;
+    bwd_load<D>(reinterpret_cast<const char*>(a.q + qhead), rs, t * kBwdTile, N, tid, stq);
+    bwd_load<D>(reinterpret_cast<const char*>(a.dout + qhead), rs, t * kBwdTile, N, tid, sto);
+    if (tid < 2 * kBwdTile) {
+      const int r = t * kBwdTile + (tid & (kBwdTile - 1));
+      const long long idx = (long long)bh * N + min(r, N - 1);
+      lsd = tid < kBwdTile ? a.lse[idx] * kLog2e : a.dsum[idx];
+    }
+  };
+  load_step(0);
+  for (int s = 0; s < n_steps; s++) {
+    const int t = t0 + s % (n_qt - t0);
+    if (s > 0) __syncthreads();
+    bwd_store<D>(sQ, tid, stq);
+    bwd_store<D>(sO, tid, sto);
+    if (tid < kBwdTile) sL[tid] = lsd;
+    else if (tid < 2 * kBwdTile) sD[tid - kBwdTile] = lsd;
+    __syncthreads();
+    if (s + 1 < n_steps) load_step(s + 1);
+#pragma unroll
+    for (int sb = 0; sb < 2; sb++) {
+      const int q0 = t * kBwdTile + 32 * sb;
+      if (q0 >= N || (CAUSAL && q0 + 31 < kw0)) continue;
+      f32x16 sc = f32x16{}, dp = f32x16{};
+#pragma unroll
+      for (int dk = 0; dk < DK; dk++)
+        sc = __builtin_amdgcn_mfma_f32_32x32x16_bf16(bwd_row<D>(sQ, 32 * sb + c, dk, h), kf[dk], sc, 0, 0, 0);
+#pragma unroll
+      for (int dk = 0; dk < DK; dk++)
+        dp = __builtin_amdgcn_mfma_f32_32x32x16_bf16(bwd_row<D>(sO, 32 * sb + c, dk, h), vf[dk], dp, 0, 0, 0);
+      // rows of the accumulators are queries 32 sb + acc_row(i, h); L and D of those from LDS
+      float l2[16], dd[16];
+#pragma unroll
+      for (int j4 = 0; j4 < 4; j4++) {
+        const f32x4v lv = *(const FA_LDS f32x4v*)(&sL[32 * sb + 8 * j4 + 4 * h]);
+        const f32x4v dv = *(const FA_LDS f32x4v*)(&sD[32 * sb + 8 * j4 + 4 * h]);
+#pragma unroll
+        for (int e = 0; e < 4; e++) {
+          l2[4 * j4 + e] = lv[e];
+          dd[4 * j4 + e] = dv[e];
+        }
+      }
+      const bool edge = (CAUSAL && q0 < kw0 + 31) || q0 + 31 >= N;
+      bf16x8 pf[2], dsf[2];
+#pragma unroll
+      for (int i = 0; i < 16; i++) {
+        float p = fast_exp2(__builtin_fmaf(sc[i], a.scale_log2, -l2[i]));
+        if (edge) {
+          const int qi = q0 + acc_row(i, h);
+          if (qi >= N || (CAUSAL && krow > qi)) p = 0.f;
+        }
+        pf[i >> 3][i & 7] = (bf16)p;
+        dsf[i >> 3][i & 7] = (bf16)(p * (dp[i] - dd[i]));
+      }
+#pragma unroll
+      for (int ks = 0; ks < 2; ks++)
+#pragma unroll
+        for (int db = 0; db < DB; db++) {
+          accv[db] = __builtin_amdgcn_mfma_f32_32x32x16_bf16(bwd_tr<D>(sO, 32 * sb + 16 * ks, db, lane),
+                                                             pf[ks], accv[db], 0, 0, 0);
+          acck[db] = __builtin_amdgcn_mfma_f32_32x32x16_bf16(bwd_tr<D>(sQ, 32 * sb + 16 * ks, db, lane),
+                                                             dsf[ks], acck[db], 0, 0, 0);
+        }
+    }
+  }
+
+  if (krow < N) {
+    bf16* dkr = a.dk + kvoff;
+    bf16* dvr = a.dv + kvoff;
+#pragma unroll
+    for (int db = 0; db < DB; db++)
+#pragma unroll
+      for (int g4 = 0; g4 < 4; g4++) {
+        bf16x4 k4, v4;
+#pragma unroll
+        for (int e = 0; e < 4; e++) {
+          k4[e] = (bf16)(acck[db][4 * g4 + e] * a.scale);
+          v4[e] = (bf16)accv[db][4 * g4 + e];
+        }
+        *reinterpret_cast<bf16x4*>(dkr + 32 * db + 8 * g4 + 4 * h) = k4;
+        *reinterpret_cast<bf16x4*>(dvr + 32 * db + 8 * g4 + 4 * h) = v4;
+      }
+  }
+}
+
+}  // namespace fa

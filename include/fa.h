@@ -129,6 +129,33 @@ int fa_fwd_splitkv(const void* q, const void* k, const void* v, void* o, float* 
                    int layout, int n_splits, void* workspace, size_t workspace_bytes,
                    void* stream);
 
+/*
+ * Backward pass by recomputation ("Understanding FlashAttention Pt 1", §3.6; "Online Softmax &
+ * FlashAttention", §26.4; the logsumexp form of the probabilities from "FlashAttention-2 -- Deeper
+ * Math", Fix 2). Given the forward's inputs q, k, v, its output o and logsumexp lse (as written by
+ * fa_fwd / fa_fwd_gqa for the same scale, mask and layout) and the upstream gradient dout = dL/dO,
+ * writes the gradients of L:
+ *     P = exp(scale q k^T - lse) (masked entries 0),   dV = P^T dout,   dP = dout v^T,
+ *     D = rowsum(dout * o),   dS = P * (dP - D),   dQ = scale dS k,   dK = scale dS^T q.
+ * With grouped K/V heads (H_kv < H) a K/V head's dk and dv are the sums over the query heads
+ * that use it (query head h uses K/V head h / (H / H_kv)).
+ *
+ * fa_bwd_workspace_bytes -- bytes of device workspace fa_bwd needs: B * H * N floats (D). Returns
+ *   0 for an invalid shape.
+ * fa_bwd -- bf16 q, k, v, o, dout, dq, dk, dv in `layout` (q, o, dout, dq: H heads; k, v, dk, dv:
+ *   H_kv heads; shapes as fa_fwd_gqa); fp32 lse [B][H][N]; fp32 arithmetic with the probabilities
+ *   and dS rounded to bf16 as matrix-core operands. `workspace`: caller-owned device memory of at
+ *   least fa_bwd_workspace_bytes(B, H, N) bytes, contents on entry irrelevant. Outputs must not
+ *   overlap any input, each other or the workspace; all pointers 16-byte aligned. Two kernels are
+ *   enqueued on `stream`; calls that share a workspace must not overlap. The result is
+ *   deterministic (no atomics). Limits and return codes as fa_fwd_gqa (d in {64, 128}).
+ */
+size_t fa_bwd_workspace_bytes(int B, int H, int N);
+int fa_bwd(const void* q, const void* k, const void* v, const void* o, const void* dout,
+           const float* lse, void* dq, void* dk, void* dv, int B, int H, int H_kv, int N, int d,
+           float scale, int causal, int layout, void* workspace, size_t workspace_bytes,
+           void* stream);
+
 /* Human-readable text for a return code (static storage; never NULL). */
 const char* fa_strerror(int code);
 

@@ -26,9 +26,9 @@ def _codes():
 
 
 def test_header_declares_the_expected_entry_points():
-    assert _declared() == ["fa_fwd", "fa_fwd_f32", "fa_fwd_gqa", "fa_fwd_gqa_f32",
-                           "fa_fwd_splitkv", "fa_splitkv_workspace_bytes", "fa_strerror",
-                           "fa_version"]
+    assert _declared() == ["fa_bwd", "fa_bwd_workspace_bytes", "fa_fwd", "fa_fwd_f32",
+                           "fa_fwd_gqa", "fa_fwd_gqa_f32", "fa_fwd_splitkv",
+                           "fa_splitkv_workspace_bytes", "fa_strerror", "fa_version"]
 
 
 def test_library_exports_every_declared_symbol():
@@ -207,3 +207,61 @@ def test_splitkv_workspace_bytes():
     assert f(1, 8, 2, 9, 4096, 128, 1, 0) == 0          # 36 rows per K/V head: not accepted
     assert f(1, 8, 3, 1, 4096, 128, 1, 0) == 0          # uneven head groups
     assert f(1, 8, 2, 1, 40, 128, 1, 1000) == f(1, 8, 2, 1, 40, 128, 1, 2)  # at most 1 split / 32 keys
+
+
+# ---- backward ------------------------------------------------------------------------------------
+DO_, DQ_, DK_, DV_, WB_ = (A + (9 + i) * (1 << 32) for i in range(5))
+GOOD_BWD = dict(q=Q, k=K, v=V, o=O, do=DO_, lse=L, dq=DQ_, dk=DK_, dv=DV_, B=2, H=8, H_kv=2,
+                N=300, d=128, scale=0.1, causal=1, layout=0, ws=WB_, ws_bytes=1 << 30)
+
+
+def _call_bwd(**kw):
+    a = dict(GOOD_BWD, **kw)
+    return fa.fa_bwd(a["q"], a["k"], a["v"], a["o"], a["do"], a["lse"], a["dq"], a["dk"], a["dv"],
+                     a["B"], a["H"], a["H_kv"], a["N"], a["d"], a["scale"], a["causal"],
+                     a["layout"], a["ws"], a["ws_bytes"], None)
+
+
+BAD_BWD = [
+    (dict(ws=0), fa.FA_ERR_INVALID_ARG),
+    (dict(do=0), fa.FA_ERR_INVALID_ARG),
+    (dict(dk=0), fa.FA_ERR_INVALID_ARG),
+    (dict(o=0), fa.FA_ERR_INVALID_ARG),
+    (dict(ws_bytes=2 * 8 * 300 * 4 - 1), fa.FA_ERR_INVALID_ARG),  # one byte short of B*H*N floats
+    (dict(N=0), fa.FA_ERR_INVALID_ARG),
+    (dict(H_kv=3), fa.FA_ERR_INVALID_ARG),
+    (dict(layout=2), fa.FA_ERR_INVALID_ARG),
+    (dict(causal=-1), fa.FA_ERR_INVALID_ARG),
+    (dict(scale=-1.0), fa.FA_ERR_INVALID_ARG),
+    (dict(d=256), fa.FA_ERR_UNSUPPORTED),
+    (dict(dq=DQ_ + 4), fa.FA_ERR_ALIGNMENT),
+    (dict(do=DO_ + 2), fa.FA_ERR_ALIGNMENT),
+    (dict(dq=Q), fa.FA_ERR_INVALID_ARG),      # dq overlaps q
+    (dict(dv=DO_), fa.FA_ERR_INVALID_ARG),    # dv overlaps dout
+    (dict(dk=DV_), fa.FA_ERR_INVALID_ARG),    # dk overlaps dv
+    (dict(ws=L), fa.FA_ERR_INVALID_ARG),      # workspace overlaps lse
+]
+
+
+@pytest.mark.parametrize("kw,code", BAD_BWD, ids=[str(b[0]) for b in BAD_BWD])
+def test_bad_backward_arguments_are_refused(kw, code):
+    assert _call_bwd(**kw) == code
+
+
+def test_backward_workspace_bytes():
+    assert fa.fa_bwd_workspace_bytes(2, 8, 300) == 2 * 8 * 300 * 4
+    assert fa.fa_bwd_workspace_bytes(0, 8, 300) == 0
+    assert fa.fa_bwd_workspace_bytes(1, 1, (1 << 22) + 1) == 0
+
+
+def test_backward_binding_checks_tensors_before_calling():
+    q = torch.zeros(1, 2, 8, 64, dtype=torch.bfloat16)
+    lse = torch.zeros(1, 2, 8)
+    with pytest.raises(ValueError):
+        fa.backward(q, q, q, q, lse, q, layout="bnhd ")
+    with pytest.raises(ValueError):
+        fa.backward(q, q, q, q, lse.double(), q)   # lse must be float32
+    with pytest.raises(ValueError):
+        fa.backward(q, q, q, q[:, :, :4].contiguous(), lse, q)  # o's shape differs from q's
+    with pytest.raises(ValueError):
+        fa.backward(q, q, q, q, lse, q)  # CPU tensors (shapes are fine)
