@@ -178,6 +178,95 @@ def bench_decode(args, w):
     print(json.dumps(rec), flush=True)
 
 
+def bench_backward(args, w):
+    """Backward workloads: one step = one fa_bwd call (the dQ kernel, then the dK/dV kernel), with
+    O and the logsumexp from one forward call and the workspace allocated before the timed
+    region. Reported in TFLOP/s of the five gradient products (10*B*H*N^2*d, halved if causal)."""
+    import numpy as np
+    import torch
+    import exact_tiled_attention_05_amd as fa
+    from exact_tiled_attention_05_amd import workloads as W
+    from oracle import attention_backward_head
+
+    causal = w["causal"][-1]
+    q, k, v, scale = W.workload_inputs(args.workload)
+    do = W.workload_grad(args.workload)
+    B, H, N, d = w["B"], w["H"], w["N"], w["d"]
+    H_kv = w.get("H_kv", H)
+    layout = w.get("layout", "bhnd")
+    lay = fa.FA_LAYOUT_BHND if layout == "bhnd" else fa.FA_LAYOUT_BNHD
+    dev = torch.device("cuda:0")
+    qd, kd, vd, dod = (W.to_layout(x, layout).to(dev) for x in (q, k, v, do))
+    o, lse = fa.forward(qd, kd, vd, scale=scale, causal=causal, layout=layout)
+    dq, dk, dv = torch.empty_like(qd), torch.empty_like(kd), torch.empty_like(vd)
+    need = fa.fa_bwd_workspace_bytes(B, H, N)
+    ws = torch.empty(need, dtype=torch.uint8, device=dev)
+    stream = torch.cuda.current_stream(dev)
+    argv = (qd.data_ptr(), kd.data_ptr(), vd.data_ptr(), o.data_ptr(), dod.data_ptr(),
+            lse.data_ptr(), dq.data_ptr(), dk.data_ptr(), dv.data_ptr(), B, H, H_kv, N, d, scale,
+            int(causal), lay, ws.data_ptr(), need, stream.cuda_stream)
+
+    def step():
+        rc = fa.fa_bwd(*argv)
+        if rc != fa.FA_OK:
+            raise fa.FAError(rc, "fa_bwd")
+
+    for _ in range(args.warmup):
+        step()
+    torch.cuda.synchronize()
+    e0 = torch.cuda.Event(enable_timing=True)
+    e1 = torch.cuda.Event(enable_timing=True)
+    t0 = time.perf_counter()
+    e0.record(stream)
+    for _ in range(args.steps):
+        step()
+    e1.record(stream)
+    torch.cuda.synchronize()
+    wall = time.perf_counter() - t0
+    ms = e0.elapsed_time(e1) / args.steps
+    flops = W.metric_flops_bwd(B, H, N, d, causal)
+    tflops = flops / (ms * 1e-3) / 1e12
+    rec = {
+        "metric": "attention bwd TFLOP/s (10*B*H*N^2*d, 1/2 if causal)",
+        "value": round(tflops, 2), "unit": "TFLOP/s", "n_gpus": 1, "steps": args.steps,
+        "warmup": args.warmup, "ms_per_step": round(ms, 5), "higher_is_better": True,
+        "scaling": "weak", "vs_baseline": None, "dtype": "bf16",
+        "data": "synthetic (seeded N(0,1) Q, K, V, dO)",
+        "config": {"workload": args.workload, "B": B, "H": H, "H_kv": H_kv, "N": N, "d": d,
+                   "causal": causal, "layout": layout,
+                   "kernel": "fa_bwd (fa_bwd_dq_kernel + fa_bwd_dkdv_kernel)",
+                   "workspace_bytes": need},
+        "roofline": {"bound": "mfma", "achieved": round(tflops, 2), "peak": PEAK_BF16_TFLOPS,
+                     "unit": "TFLOP/s", "frac": round(tflops / PEAK_BF16_TFLOPS, 4),
+                     "traffic": recorded_traffic(args.workload)},
+        "wall_s_timed_region": round(wall, 4),
+    }
+    if not args.no_cpu:
+        try:
+            from threadpoolctl import threadpool_info
+            threads = max([i.get("num_threads", 1) for i in threadpool_info()
+                           if i.get("user_api") == "blas"] or [1])
+        except Exception:  # pragma: no cover
+            threads = 1
+        group = H // H_kv
+        dt, done = 0.0, 0
+        for h in range(H):
+            qh, doh = (x[0, h].float().numpy().astype(np.float64) for x in (q, do))
+            kh, vh = (x[0, h // group].float().numpy().astype(np.float64) for x in (k, v))
+            t1 = time.perf_counter()
+            attention_backward_head(qh, kh, vh, doh, scale, causal)
+            dt += time.perf_counter() - t1
+            done += 1
+            if dt >= 15.0:
+                break
+        cflops = W.metric_flops_bwd(1, done, N, d, causal)
+        rec["cpu_baseline"] = {"value": cflops / dt / 1e12, "unit": "TFLOP/s", "cores": threads,
+                               "kind": "oracle",
+                               "sample": "%d of %d heads of batch 0, every row (numpy float64, "
+                                         "dense S, P, dP, dS), %.1f s" % (done, B * H, dt)}
+    print(json.dumps(rec), flush=True)
+
+
 def kernel_source_digest():
     """sha256 over the HIP sources and build flags of libfa.so (identifies the kernel build)."""
     import hashlib
@@ -226,6 +315,8 @@ def main():
     w = W.WORKLOADS[args.workload]
     if "Nq" in w:
         return bench_decode(args, w)
+    if w.get("backward"):
+        return bench_backward(args, w)
     causal = w["causal"][-1]
     q, k, v, scale = W.workload_inputs(args.workload)
     layout = w.get("layout", "bhnd")

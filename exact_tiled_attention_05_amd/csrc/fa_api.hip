@@ -194,10 +194,10 @@ template <int D, bool CAUSAL>
 hipError_t launch_bwd(fa::BwdArgs a, hipStream_t s) {
   void* args[] = {&a};
   hipError_t e = hipLaunchKernel(reinterpret_cast<const void*>(&fa::fa_bwd_dq_kernel<D, CAUSAL>),
-                                 dim3(a.n_qblk * a.BH), dim3(fa::kBwdWaves * 64), args, 0, s);
+                                 dim3(a.n_qblk * a.BH), dim3(fa::kBwdQWaves * 64), args, 0, s);
   if (e != hipSuccess) return e;
   return hipLaunchKernel(reinterpret_cast<const void*>(&fa::fa_bwd_dkdv_kernel<D, CAUSAL>),
-                         dim3(a.n_kblk * a.BHkv), dim3(fa::kBwdWaves * 64), args, 0, s);
+                         dim3(a.n_kblk * a.BHkv), dim3(fa::kBwdKvWaves * 64), args, 0, s);
 }
 
 }  // namespace
@@ -252,8 +252,8 @@ int fa_bwd(const void* q, const void* k, const void* v, const void* o, const voi
   a.group = H / H_kv;
   a.BH = B * H;
   a.BHkv = B * H_kv;
-  a.n_qblk = (N + fa::kBwdRows - 1) / fa::kBwdRows;
-  a.n_kblk = a.n_qblk;
+  a.n_qblk = (N + fa::kBwdQRows - 1) / fa::kBwdQRows;
+  a.n_kblk = (N + fa::kBwdKvRows - 1) / fa::kBwdKvRows;
   a.scale = scale;
   a.scale_log2 = scale * fa::kLog2e;
   const Strides sq = strides_of(layout, H, N, d), sk = strides_of(layout, H_kv, N, d);

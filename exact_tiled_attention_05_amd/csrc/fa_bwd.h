@@ -16,7 +16,7 @@
 //     S^T = K Q^T, dP^T = V dO^T (keys on M, queries on N, as in the forward kernel), P^T and dS^T
 //     in fp32, then dQ^T += K^T dS^T with dS^T rounded to bf16 as the B operand and K^T read
 //     with the transposing LDS read.
-//   fa_bwd_dkdv_kernel (keys outermost): 4 waves x 32 keys per workgroup. A wave keeps its keys'
+//   fa_bwd_dkdv_kernel (keys outermost): 8 waves x 32 keys per workgroup (two per SIMD). A wave keeps its keys'
 //     K and V rows in registers as B operands and loops over the query tiles -- of every query
 //     head that shares the K/V head, so grouped heads receive the sum of their query heads'
 //     gradients -- with Q, dO, L and D of each 64-query tile in LDS: S = Q K^T, dP = dO V^T
@@ -34,9 +34,11 @@
 
 namespace fa {
 
-constexpr int kBwdWaves = 4;
-constexpr int kBwdRows = 32 * kBwdWaves;  // query rows (dQ kernel) or keys (dK/dV kernel) per workgroup
-constexpr int kBwdTile = 64;              // rows of a K/V tile (dQ kernel) or a Q/dO tile (dK/dV kernel)
+constexpr int kBwdQWaves = 4;                 // dQ kernel: waves per workgroup
+constexpr int kBwdQRows = 32 * kBwdQWaves;    // query rows per dQ workgroup
+constexpr int kBwdKvWaves = 8;                // dK/dV kernel: waves per workgroup
+constexpr int kBwdKvRows = 32 * kBwdKvWaves;  // keys per dK/dV workgroup
+constexpr int kBwdTile = 64;  // rows of a K/V tile (dQ kernel) or a Q/dO tile (dK/dV kernel)
 
 typedef unsigned int u32x4v __attribute__((ext_vector_type(4)));
 typedef float f32x4v __attribute__((ext_vector_type(4)));
@@ -66,47 +68,51 @@ struct Swz {
   static constexpr int ROW = 2 * D;  // bytes per row
   static constexpr int CPR = D / 8;  // 16-byte chunks per row
   static constexpr int BYTES = kBwdTile * ROW;
-  // d = 128 (16 chunks): row reads need f injective on 16 consecutive rows; the transposing read
-  // of rows 8u..8u+7 x chunks 4b..4b+3 needs (chunk ^ f) to hit each of the 16 positions twice:
-  // f(r) = 2 (r mod 8) + bit 3 of r does both. d = 64 (8 chunks, two rows per 256 bytes): f is a
-  // bit permutation of r / 2 that puts bits 1 and 2 of r on chunk bits 0 and 2.
+  // The LDS serves a 16-byte row read 16 lanes at a time (16 consecutive rows, one chunk each)
+  // and a transposing 8-byte read 32 lanes at a time (4 consecutive rows x 4 chunks of one
+  // 4-chunk group). d = 128 (16 chunks per 256-byte row): f must be injective on 16 consecutive
+  // rows, and 4 consecutive rows must move a chunk group to 4 different groups (f / 4 distinct):
+  // f(r) = 4 (r mod 4) + (r / 4) mod 4. d = 64 (8 chunks, two rows per 256 bytes): rows of equal
+  // parity share banks, so f must be injective on the 8 rows of one parity among 16, and rows r,
+  // r+2 must use different halves (bit 2 of f): f(r) = 4 ((r / 2) mod 2) + (r / 4) mod 4. Both
+  // also keep the staging writes (whole rows) conflict-free.
   __device__ static __forceinline__ int f(int r) {
-    if constexpr (D == 128) return ((r & 7) << 1) | ((r >> 3) & 1);
-    else return ((r >> 1) & 1) | (((r >> 3) & 1) << 1) | (((r >> 2) & 1) << 2);
+    if constexpr (D == 128) return ((r & 3) << 2) | ((r >> 2) & 3);
+    else return (((r >> 1) & 1) << 2) | ((r >> 2) & 3);
   }
   __device__ static __forceinline__ int off(int r, int j) { return r * ROW + 16 * (j ^ f(r)); }
 };
 
-// One 64-row tile staged in registers: 256 threads, each one 16-byte chunk per piece.
-template <int D>
+// One 64-row tile staged in registers by T threads, each one 16-byte chunk per piece.
+template <int D, int T>
 struct BwdStage {
-  static constexpr int PIECES = kBwdTile * Swz<D>::CPR / 256;
-  static constexpr int RPP = 256 / Swz<D>::CPR;  // rows per piece
+  static constexpr int PIECES = kBwdTile * Swz<D>::CPR / T;
+  static constexpr int RPP = T / Swz<D>::CPR;  // rows per piece
   u32x4v r[PIECES];
 };
 
 // Rows row0 .. row0+63 of one head (rows at byte stride rs) into registers; rows at or past N read
 // as zeros (the buffer resource ends at row N-1).
-template <int D>
+template <int D, int T>
 __device__ __forceinline__ void bwd_load(const char* head, long long rs, int row0, int N, int tid,
-                                         BwdStage<D>& st) {
+                                         BwdStage<D, T>& st) {
   constexpr int CPR = Swz<D>::CPR;
   const int rows = min(N - row0, kBwdTile);  // >= 1: only tiles that start below N are loaded
   const __amdgpu_buffer_rsrc_t r = __builtin_amdgcn_make_buffer_rsrc(
       (void*)(head + (long long)row0 * rs), 0, (int)((rows - 1) * rs) + 2 * D, 0x00020000);
   const int voff = (int)((tid / CPR) * rs) + 16 * (tid % CPR);
 #pragma unroll
-  for (int i = 0; i < BwdStage<D>::PIECES; i++)
+  for (int i = 0; i < BwdStage<D, T>::PIECES; i++)
     st.r[i] = __builtin_bit_cast(
-        u32x4v, __builtin_amdgcn_raw_buffer_load_b128(r, voff, (int)(i * BwdStage<D>::RPP * rs), 0));
+        u32x4v, __builtin_amdgcn_raw_buffer_load_b128(r, voff, (int)(i * BwdStage<D, T>::RPP * rs), 0));
 }
 
-template <int D>
-__device__ __forceinline__ void bwd_store(char* tile, int tid, const BwdStage<D>& st) {
+template <int D, int T>
+__device__ __forceinline__ void bwd_store(char* tile, int tid, const BwdStage<D, T>& st) {
   constexpr int CPR = Swz<D>::CPR;
 #pragma unroll
-  for (int i = 0; i < BwdStage<D>::PIECES; i++) {
-    const int slot = i * 256 + tid;
+  for (int i = 0; i < BwdStage<D, T>::PIECES; i++) {
+    const int slot = i * T + tid;
     *(FA_LDS u32x4v*)(tile + Swz<D>::off(slot / CPR, slot % CPR)) = st.r[i];
   }
 }
@@ -136,7 +142,7 @@ __device__ __forceinline__ constexpr int acc_row(int i, int h) { return 8 * (i >
 // dQ (and D)
 // ---------------------------------------------------------------------------------------------
 template <int D, bool CAUSAL>
-__global__ __launch_bounds__(256) __attribute__((amdgpu_waves_per_eu(2))) void fa_bwd_dq_kernel(BwdArgs a) {
+__global__ __launch_bounds__(kBwdQWaves * 64) __attribute__((amdgpu_waves_per_eu(2))) void fa_bwd_dq_kernel(BwdArgs a) {
   constexpr int DK = D / 16, DB = D / 32;
   using S = Swz<D>;
   __shared__ __attribute__((aligned(1024))) char sK[S::BYTES];
@@ -148,7 +154,7 @@ __global__ __launch_bounds__(256) __attribute__((amdgpu_waves_per_eu(2))) void f
   map_block<CAUSAL>(blockIdx.x, gridDim.x, a.BH, a.n_qblk, bh, qblk);
   const int b = bh / a.H, hq = bh - b * a.H, hk = hq / a.group;
   const int N = a.N;
-  const int qw0 = qblk * kBwdRows + 32 * wave;
+  const int qw0 = qblk * kBwdQRows + 32 * wave;
   const int qrow = qw0 + c;
   const long long qoff = b * a.q_bs + hq * a.q_hs + (long long)qrow * a.q_rs;
   const long long kvhead = b * a.kv_bs + hk * a.kv_hs;
@@ -183,22 +189,23 @@ __global__ __launch_bounds__(256) __attribute__((amdgpu_waves_per_eu(2))) void f
   for (int db = 0; db < DB; db++) acc[db] = f32x16{};
 
   const int wave_last = CAUSAL ? min(N - 1, qw0 + 31) : N - 1;  // last key this wave needs
-  const int blk_last = CAUSAL ? min(N - 1, qblk * kBwdRows + kBwdRows - 1) : N - 1;
+  const int blk_last = CAUSAL ? min(N - 1, qblk * kBwdQRows + kBwdQRows - 1) : N - 1;
   const int n_kt = blk_last / kBwdTile + 1;
   const char* kh = reinterpret_cast<const char*>(a.k + kvhead);
   const char* vh = reinterpret_cast<const char*>(a.v + kvhead);
-  BwdStage<D> stk, stv;
-  bwd_load<D>(kh, rs, 0, N, tid, stk);
-  bwd_load<D>(vh, rs, 0, N, tid, stv);
+  constexpr int T = kBwdQWaves * 64;
+  BwdStage<D, T> stk, stv;
+  bwd_load<D, T>(kh, rs, 0, N, tid, stk);
+  bwd_load<D, T>(vh, rs, 0, N, tid, stv);
 
   for (int j = 0; j < n_kt; j++) {
     if (j > 0) __syncthreads();  // every wave is done with tile j-1
-    bwd_store<D>(sK, tid, stk);
-    bwd_store<D>(sV, tid, stv);
+    bwd_store<D, T>(sK, tid, stk);
+    bwd_store<D, T>(sV, tid, stv);
     __syncthreads();
     if (j + 1 < n_kt) {
-      bwd_load<D>(kh, rs, (j + 1) * kBwdTile, N, tid, stk);
-      bwd_load<D>(vh, rs, (j + 1) * kBwdTile, N, tid, stv);
+      bwd_load<D, T>(kh, rs, (j + 1) * kBwdTile, N, tid, stk);
+      bwd_load<D, T>(vh, rs, (j + 1) * kBwdTile, N, tid, stv);
     }
 #pragma unroll
     for (int sb = 0; sb < 2; sb++) {
@@ -250,13 +257,15 @@ __global__ __launch_bounds__(256) __attribute__((amdgpu_waves_per_eu(2))) void f
 // dK, dV
 // ---------------------------------------------------------------------------------------------
 template <int D, bool CAUSAL>
-__global__ __launch_bounds__(256) __attribute__((amdgpu_waves_per_eu(1, 1))) void fa_bwd_dkdv_kernel(BwdArgs a) {
+__global__ __launch_bounds__(kBwdKvWaves * 64) __attribute__((amdgpu_waves_per_eu(2))) void fa_bwd_dkdv_kernel(BwdArgs a) {
   constexpr int DK = D / 16, DB = D / 32;
+  constexpr int T = kBwdKvWaves * 64;
   using S = Swz<D>;
   __shared__ __attribute__((aligned(1024))) char sQ[S::BYTES];
   __shared__ __attribute__((aligned(1024))) char sO[S::BYTES];  // dO
   __shared__ __attribute__((aligned(16))) float sL[kBwdTile];    // L * log2(e)
   __shared__ __attribute__((aligned(16))) float sD[kBwdTile];    // D
+  __shared__ __attribute__((aligned(1024))) char sVb[kBwdKvRows * S::ROW];  // this block's V rows
 
   const int tid = threadIdx.x, wave = tid >> 6, lane = tid & 63;
   const int c = lane & 31, h = lane >> 5;
@@ -266,16 +275,20 @@ __global__ __launch_bounds__(256) __attribute__((amdgpu_waves_per_eu(1, 1))) voi
                                                    // most queries, first
   const int b = bkv / a.Hkv, hk = bkv - b * a.Hkv;
   const int N = a.N;
-  const int kw0 = kblk * kBwdRows + 32 * wave;
+  const int kw0 = kblk * kBwdKvRows + 32 * wave;
   const int krow = kw0 + c;
   const long long kvoff = b * a.kv_bs + hk * a.kv_hs + (long long)krow * a.kv_rs;
   const long long rs = 2LL * a.q_rs;
 
-  bf16x8 kf[DK], vf[DK];
+  // K rows of this lane's key as the B operand of S = Q K^T, in registers for the whole kernel.
+  // V rows (the B operand of dP = dO V^T) go to LDS once and are read per step: keeping both in
+  // registers as well as the two accumulators does not fit two waves per SIMD.
+  bf16x8 kf[DK];
 #pragma unroll
   for (int dk = 0; dk < DK; dk++) {
     kf[dk] = krow < N ? *reinterpret_cast<const bf16x8*>(a.k + kvoff + dk * 16 + h * 8) : bf16x8{};
-    vf[dk] = krow < N ? *reinterpret_cast<const bf16x8*>(a.v + kvoff + dk * 16 + h * 8) : bf16x8{};
+    const bf16x8 vv = krow < N ? *reinterpret_cast<const bf16x8*>(a.v + kvoff + dk * 16 + h * 8) : bf16x8{};
+    *(FA_LDS bf16x8*)(sVb + S::off(32 * wave + c, 2 * dk + h)) = vv;
   }
   f32x16 acck[DB], accv[DB];
 #pragma unroll
@@ -284,17 +297,17 @@ __global__ __launch_bounds__(256) __attribute__((amdgpu_waves_per_eu(1, 1))) voi
     accv[db] = f32x16{};
   }
 
-  const int t0 = CAUSAL ? (kblk * kBwdRows) / kBwdTile : 0;  // first query tile with a visible key
+  const int t0 = CAUSAL ? (kblk * kBwdKvRows) / kBwdTile : 0;  // first query tile with a visible key
   const int n_qt = (N + kBwdTile - 1) / kBwdTile;
   const int n_steps = a.group * (n_qt - t0);  // (query head, query tile) pairs, in that order
-  BwdStage<D> stq, sto;
+  BwdStage<D, T> stq, sto;
   float lsd = 0.f;
   auto load_step = [&](int s) {
     const int g = s / (n_qt - t0), t = t0 + s % (n_qt - t0);
     const int bh = b * a.H + hk * a.group + g;
     const long long qhead = b * a.q_bs + (long long)(hk * a.group + g) * a.q_hs;
-    bwd_load<D>(reinterpret_cast<const char*>(a.q + qhead), rs, t * kBwdTile, N, tid, stq);
-    bwd_load<D>(reinterpret_cast<const char*>(a.dout + qhead), rs, t * kBwdTile, N, tid, sto);
+    bwd_load<D, T>(reinterpret_cast<const char*>(a.q + qhead), rs, t * kBwdTile, N, tid, stq);
+    bwd_load<D, T>(reinterpret_cast<const char*>(a.dout + qhead), rs, t * kBwdTile, N, tid, sto);
     if (tid < 2 * kBwdTile) {
       const int r = t * kBwdTile + (tid & (kBwdTile - 1));
       const long long idx = (long long)bh * N + min(r, N - 1);
@@ -305,56 +318,68 @@ __global__ __launch_bounds__(256) __attribute__((amdgpu_waves_per_eu(1, 1))) voi
   for (int s = 0; s < n_steps; s++) {
     const int t = t0 + s % (n_qt - t0);
     if (s > 0) __syncthreads();
-    bwd_store<D>(sQ, tid, stq);
-    bwd_store<D>(sO, tid, sto);
+    bwd_store<D, T>(sQ, tid, stq);
+    bwd_store<D, T>(sO, tid, sto);
     if (tid < kBwdTile) sL[tid] = lsd;
     else if (tid < 2 * kBwdTile) sD[tid - kBwdTile] = lsd;
     __syncthreads();
     if (s + 1 < n_steps) load_step(s + 1);
-#pragma unroll
+#pragma unroll 1
     for (int sb = 0; sb < 2; sb++) {
       const int q0 = t * kBwdTile + 32 * sb;
       if (q0 >= N || (CAUSAL && q0 + 31 < kw0)) continue;
-      f32x16 sc = f32x16{}, dp = f32x16{};
+      const bool edge = (CAUSAL && q0 < kw0 + 31) || q0 + 31 >= N;
+      // S = Q K^T, then P (rows: queries 32 sb + acc_row(i, h); L of those from LDS) and its
+      // bf16 copy, then dV^T += dO^T P -- so S and the bf16 P are dead before dP is formed.
+      f32x16 sc = f32x16{};
 #pragma unroll
       for (int dk = 0; dk < DK; dk++)
         sc = __builtin_amdgcn_mfma_f32_32x32x16_bf16(bwd_row<D>(sQ, 32 * sb + c, dk, h), kf[dk], sc, 0, 0, 0);
-#pragma unroll
-      for (int dk = 0; dk < DK; dk++)
-        dp = __builtin_amdgcn_mfma_f32_32x32x16_bf16(bwd_row<D>(sO, 32 * sb + c, dk, h), vf[dk], dp, 0, 0, 0);
-      // rows of the accumulators are queries 32 sb + acc_row(i, h); L and D of those from LDS
-      float l2[16], dd[16];
+      float p[16];
+      bf16x8 pf[2];
 #pragma unroll
       for (int j4 = 0; j4 < 4; j4++) {
         const f32x4v lv = *(const FA_LDS f32x4v*)(&sL[32 * sb + 8 * j4 + 4 * h]);
-        const f32x4v dv = *(const FA_LDS f32x4v*)(&sD[32 * sb + 8 * j4 + 4 * h]);
 #pragma unroll
         for (int e = 0; e < 4; e++) {
-          l2[4 * j4 + e] = lv[e];
-          dd[4 * j4 + e] = dv[e];
+          const int i = 4 * j4 + e;
+          float pi = fast_exp2(__builtin_fmaf(sc[i], a.scale_log2, -lv[e]));
+          if (edge) {
+            const int qi = q0 + acc_row(i, h);
+            if (qi >= N || (CAUSAL && krow > qi)) pi = 0.f;
+          }
+          p[i] = pi;
+          pf[i >> 3][i & 7] = (bf16)pi;
         }
-      }
-      const bool edge = (CAUSAL && q0 < kw0 + 31) || q0 + 31 >= N;
-      bf16x8 pf[2], dsf[2];
-#pragma unroll
-      for (int i = 0; i < 16; i++) {
-        float p = fast_exp2(__builtin_fmaf(sc[i], a.scale_log2, -l2[i]));
-        if (edge) {
-          const int qi = q0 + acc_row(i, h);
-          if (qi >= N || (CAUSAL && krow > qi)) p = 0.f;
-        }
-        pf[i >> 3][i & 7] = (bf16)p;
-        dsf[i >> 3][i & 7] = (bf16)(p * (dp[i] - dd[i]));
       }
 #pragma unroll
       for (int ks = 0; ks < 2; ks++)
 #pragma unroll
-        for (int db = 0; db < DB; db++) {
+        for (int db = 0; db < DB; db++)
           accv[db] = __builtin_amdgcn_mfma_f32_32x32x16_bf16(bwd_tr<D>(sO, 32 * sb + 16 * ks, db, lane),
                                                              pf[ks], accv[db], 0, 0, 0);
+      // dP = dO V^T, dS = P (dP - D), then dK^T += Q^T dS
+      f32x16 dp = f32x16{};
+#pragma unroll
+      for (int dk = 0; dk < DK; dk++)
+        dp = __builtin_amdgcn_mfma_f32_32x32x16_bf16(bwd_row<D>(sO, 32 * sb + c, dk, h),
+                                                     bwd_row<D>(sVb, 32 * wave + c, dk, h), dp, 0, 0, 0);
+      bf16x8 dsf[2];
+#pragma unroll
+      for (int j4 = 0; j4 < 4; j4++) {
+        const f32x4v dv = *(const FA_LDS f32x4v*)(&sD[32 * sb + 8 * j4 + 4 * h]);
+#pragma unroll
+        for (int e = 0; e < 4; e++) {
+          const int i = 4 * j4 + e;
+          dsf[i >> 3][i & 7] = (bf16)(p[i] * (dp[i] - dv[e]));
+        }
+      }
+#pragma unroll
+      for (int ks = 0; ks < 2; ks++)
+#pragma unroll
+        for (int db = 0; db < DB; db++)
           acck[db] = __builtin_amdgcn_mfma_f32_32x32x16_bf16(bwd_tr<D>(sQ, 32 * sb + 16 * ks, db, lane),
                                                              dsf[ks], acck[db], 0, 0, 0);
-        }
     }
   }
 

@@ -19,7 +19,9 @@ heads over 8 K/V heads, "Understanding FlashAttention Pt 1", §4.1) in the token
 [B][N][heads][d] layout of that section; K and V are then drawn with H_kv heads. A seventh is that
 layer decoding: one new query token per sequence (Nq = 1) against N = 32768 cached keys, for a
 batch of 8 sequences ("FlashAttention-2 -- Deeper Math", "What FA-2 does not fix"); Q is then drawn
-with Nq rows.
+with Nq rows. The two "_bwd" workloads are the Llama layer (with and without grouped K/V heads)
+run backward ("Understanding FlashAttention Pt 1", §3.6): the same Q, K, V recipe and seeds as the
+forward workloads, plus an upstream gradient dO drawn like Q from its own seed.
 """
 import math
 
@@ -38,6 +40,11 @@ WORKLOADS = {
                                      causal=(True,), seed=5, layout="bnhd", sample_rows=64),
     "llama3_8b_gqa_decode_b8_n32k": dict(B=8, H=32, H_kv=8, Nq=1, N=32768, d=128, dtype="bf16",
                                          causal=(True,), seed=6, layout="bnhd"),
+    "llama3_8b_n8k_causal_bwd": dict(B=1, H=32, N=8192, d=128, dtype="bf16", causal=(True,),
+                                     seed=2, grad_seed=12, backward=True),
+    "llama3_8b_gqa_n8k_causal_bwd": dict(B=1, H=32, H_kv=8, N=8192, d=128, dtype="bf16",
+                                         causal=(True,), seed=5, grad_seed=15, layout="bnhd",
+                                         backward=True),
 }
 
 _TORCH_DTYPE = {"bf16": torch.bfloat16, "fp32": torch.float32}
@@ -117,7 +124,21 @@ def workload_inputs(name):
     return q, k, v, softmax_scale(w["d"])
 
 
+def workload_grad(name):
+    """The upstream gradient dO [B, H, N, d] of a backward workload (drawn like Q)."""
+    w = WORKLOADS[name]
+    return make_inputs(w["B"], w["H"], w["N"], w["d"], dtype=w["dtype"], seed=w["grad_seed"])[0]
+
+
 def metric_flops(B, H, N, d, causal):
     """The throughput metric's FLOP count: 4*B*H*N^2*d, halved when causal."""
     f = 4.0 * B * H * N * N * d
+    return f / 2.0 if causal else f
+
+
+def metric_flops_bwd(B, H, N, d, causal):
+    """FLOP count of the backward pass: the five N x N x d products of the gradient formulas
+    (S = QK^T, dP = dO V^T, dV = P^T dO, dQ = dS K, dK = dS^T Q), 10*B*H*N^2*d, halved when
+    causal -- 2.5 times the forward's."""
+    f = 10.0 * B * H * N * N * d
     return f / 2.0 if causal else f
