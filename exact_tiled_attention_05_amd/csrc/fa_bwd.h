@@ -83,39 +83,54 @@ struct Swz {
   __device__ static __forceinline__ int off(int r, int j) { return r * ROW + 16 * (j ^ f(r)); }
 };
 
-// One 64-row tile staged in registers by T threads, each one 16-byte chunk per piece.
-template <int D, int T>
-struct BwdStage {
-  static constexpr int PIECES = kBwdTile * Swz<D>::CPR / T;
-  static constexpr int RPP = T / Swz<D>::CPR;  // rows per piece
-  u32x4v r[PIECES];
-};
+typedef int i32x4v __attribute__((ext_vector_type(4)));
 
-// Rows row0 .. row0+63 of one head (rows at byte stride rs) into registers; rows at or past N read
-// as zeros (the buffer resource ends at row N-1).
-template <int D, int T>
-__device__ __forceinline__ void bwd_load(const char* head, long long rs, int row0, int N, int tid,
-                                         BwdStage<D, T>& st) {
-  constexpr int CPR = Swz<D>::CPR;
+// Buffer resource (as four scalar registers, for the DMA instruction) over rows row0 .. N-1 of one
+// head, rows rs bytes apart, ending after row min(N, row0 + 64) - 1: bytes past it read as zeros.
+template <int D>
+__device__ __forceinline__ i32x4v tile_rsrc(const char* head, long long rs, int row0, int N) {
   const int rows = min(N - row0, kBwdTile);  // >= 1: only tiles that start below N are loaded
-  const __amdgpu_buffer_rsrc_t r = __builtin_amdgcn_make_buffer_rsrc(
-      (void*)(head + (long long)row0 * rs), 0, (int)((rows - 1) * rs) + 2 * D, 0x00020000);
-  const int voff = (int)((tid / CPR) * rs) + 16 * (tid % CPR);
-#pragma unroll
-  for (int i = 0; i < BwdStage<D, T>::PIECES; i++)
-    st.r[i] = __builtin_bit_cast(
-        u32x4v, __builtin_amdgcn_raw_buffer_load_b128(r, voff, (int)(i * BwdStage<D, T>::RPP * rs), 0));
+  const unsigned long long base = reinterpret_cast<unsigned long long>(head + (long long)row0 * rs);
+  i32x4v r;
+  r[0] = __builtin_amdgcn_readfirstlane((int)(base & 0xffffffffu));
+  r[1] = __builtin_amdgcn_readfirstlane((int)(base >> 32));
+  r[2] = __builtin_amdgcn_readfirstlane((int)((rows - 1) * rs) + 2 * D);
+  r[3] = 0x00020000;
+  return r;
 }
 
-template <int D, int T>
-__device__ __forceinline__ void bwd_store(char* tile, int tid, const BwdStage<D, T>& st) {
-  constexpr int CPR = Swz<D>::CPR;
-#pragma unroll
-  for (int i = 0; i < BwdStage<D, T>::PIECES; i++) {
-    const int slot = i * T + tid;
-    *(FA_LDS u32x4v*)(tile + Swz<D>::off(slot / CPR, slot % CPR)) = st.r[i];
-  }
+// Global memory -> LDS without registers: one 16-byte buffer load per lane whose data the
+// hardware writes at (M0 + 16 * lane), i.e. 1 KB per wave instruction (rows 4p..4p+3 of the
+// swizzled tile for d = 128, 8p..8p+7 for d = 64, at LDS offset 1 KB * p). Lane l fills tile
+// position (row, slot) = (RPP p + l / CPR, l % CPR), so it fetches chunk slot ^ f(row) of that
+// row. The load counts on vmcnt; the caller waits for it before the barrier that publishes the
+// tile. (The DMA form is written as inline assembly: the compiler would otherwise wait for it
+// before every LDS access.)
+template <int D>
+__device__ __forceinline__ void dma_piece(char* tile, const i32x4v& rsrc, long long rs, int p,
+                                          int lane) {
+  constexpr int CPR = Swz<D>::CPR, RPP = 1024 / (2 * D);
+  const int rin = lane / CPR, slot = lane % CPR;
+  const unsigned voff = (unsigned)(rin * rs) + 16u * (unsigned)(slot ^ Swz<D>::f(RPP * p + rin));
+  const unsigned soff = __builtin_amdgcn_readfirstlane((int)(RPP * p * rs));
+  const unsigned m0 = __builtin_amdgcn_readfirstlane(
+      (int)((unsigned)(size_t)(FA_LDS char*)tile + 1024u * (unsigned)p));
+  asm volatile("s_mov_b32 m0, %0\n\tbuffer_load_dwordx4 %1, %2, %3 offen lds"
+               :: "s"(m0), "v"(voff), "s"(rsrc), "s"(soff) : "memory", "m0");
 }
+
+// The 64-row tile of rows row0.. by W waves (tile bytes / 1 KB pieces, spread over the waves).
+template <int D, int W>
+__device__ __forceinline__ void dma_tile(char* tile, const char* head, long long rs, int row0,
+                                         int N, int wave, int lane) {
+  constexpr int PIECES = Swz<D>::BYTES / 1024;
+  static_assert(PIECES % W == 0, "pieces must divide over the waves");
+  const i32x4v r = tile_rsrc<D>(head, rs, row0, N);
+#pragma unroll
+  for (int i = 0; i < PIECES / W; i++) dma_piece<D>(tile, r, rs, wave + W * i, lane);
+}
+
+__device__ __forceinline__ void wait_dma() { asm volatile("s_waitcnt vmcnt(0)" ::: "memory"); }
 
 // Row operand: 8 consecutive elements (chunk 2 dk + h) of tile row r.
 template <int D>
@@ -145,8 +160,8 @@ template <int D, bool CAUSAL>
 __global__ __launch_bounds__(kBwdQWaves * 64) __attribute__((amdgpu_waves_per_eu(2))) void fa_bwd_dq_kernel(BwdArgs a) {
   constexpr int DK = D / 16, DB = D / 32;
   using S = Swz<D>;
-  __shared__ __attribute__((aligned(1024))) char sK[S::BYTES];
-  __shared__ __attribute__((aligned(1024))) char sV[S::BYTES];
+  __shared__ __attribute__((aligned(1024))) char sK2[2][S::BYTES];  // two stages of K and V tiles
+  __shared__ __attribute__((aligned(1024))) char sV2[2][S::BYTES];
 
   const int tid = threadIdx.x, wave = tid >> 6, lane = tid & 63;
   const int c = lane & 31, h = lane >> 5;
@@ -193,20 +208,21 @@ __global__ __launch_bounds__(kBwdQWaves * 64) __attribute__((amdgpu_waves_per_eu
   const int n_kt = blk_last / kBwdTile + 1;
   const char* kh = reinterpret_cast<const char*>(a.k + kvhead);
   const char* vh = reinterpret_cast<const char*>(a.v + kvhead);
-  constexpr int T = kBwdQWaves * 64;
-  BwdStage<D, T> stk, stv;
-  bwd_load<D, T>(kh, rs, 0, N, tid, stk);
-  bwd_load<D, T>(vh, rs, 0, N, tid, stv);
-
+  // Tile j sits in stage j % 2. Tile j+1 goes straight from memory into the other stage while
+  // tile j is computed (that stage's readers finished tile j-1 before the last barrier); one
+  // barrier per tile.
+  constexpr int W = kBwdQWaves;
+  dma_tile<D, W>(sK2[0], kh, rs, 0, N, wave, lane);
+  dma_tile<D, W>(sV2[0], vh, rs, 0, N, wave, lane);
+  wait_dma();
+  __syncthreads();
   for (int j = 0; j < n_kt; j++) {
-    if (j > 0) __syncthreads();  // every wave is done with tile j-1
-    bwd_store<D, T>(sK, tid, stk);
-    bwd_store<D, T>(sV, tid, stv);
-    __syncthreads();
     if (j + 1 < n_kt) {
-      bwd_load<D, T>(kh, rs, (j + 1) * kBwdTile, N, tid, stk);
-      bwd_load<D, T>(vh, rs, (j + 1) * kBwdTile, N, tid, stv);
+      dma_tile<D, W>(sK2[(j + 1) & 1], kh, rs, (j + 1) * kBwdTile, N, wave, lane);
+      dma_tile<D, W>(sV2[(j + 1) & 1], vh, rs, (j + 1) * kBwdTile, N, wave, lane);
     }
+    const char* sK = sK2[j & 1];
+    const char* sV = sV2[j & 1];
 #pragma unroll
     for (int sb = 0; sb < 2; sb++) {
       const int k0 = j * kBwdTile + 32 * sb;
@@ -237,6 +253,10 @@ __global__ __launch_bounds__(kBwdQWaves * 64) __attribute__((amdgpu_waves_per_eu
           acc[db] = __builtin_amdgcn_mfma_f32_32x32x16_bf16(bwd_tr<D>(sK, 32 * sb + 16 * ks, db, lane),
                                                             dsf[ks], acc[db], 0, 0, 0);
     }
+    if (j + 1 < n_kt) {
+      wait_dma();
+      __syncthreads();
+    }
   }
 
   if (qrow < N) {
@@ -259,12 +279,11 @@ __global__ __launch_bounds__(kBwdQWaves * 64) __attribute__((amdgpu_waves_per_eu
 template <int D, bool CAUSAL>
 __global__ __launch_bounds__(kBwdKvWaves * 64) __attribute__((amdgpu_waves_per_eu(2))) void fa_bwd_dkdv_kernel(BwdArgs a) {
   constexpr int DK = D / 16, DB = D / 32;
-  constexpr int T = kBwdKvWaves * 64;
   using S = Swz<D>;
-  __shared__ __attribute__((aligned(1024))) char sQ[S::BYTES];
-  __shared__ __attribute__((aligned(1024))) char sO[S::BYTES];  // dO
-  __shared__ __attribute__((aligned(16))) float sL[kBwdTile];    // L * log2(e)
-  __shared__ __attribute__((aligned(16))) float sD[kBwdTile];    // D
+  __shared__ __attribute__((aligned(1024))) char sQ2[2][S::BYTES];  // two stages of Q and dO tiles
+  __shared__ __attribute__((aligned(1024))) char sO2[2][S::BYTES];
+  __shared__ __attribute__((aligned(16))) float sL2[2][kBwdTile];    // L * log2(e)
+  __shared__ __attribute__((aligned(16))) float sD2[2][kBwdTile];    // D
   __shared__ __attribute__((aligned(1024))) char sVb[kBwdKvRows * S::ROW];  // this block's V rows
 
   const int tid = threadIdx.x, wave = tid >> 6, lane = tid & 63;
@@ -300,30 +319,40 @@ __global__ __launch_bounds__(kBwdKvWaves * 64) __attribute__((amdgpu_waves_per_e
   const int t0 = CAUSAL ? (kblk * kBwdKvRows) / kBwdTile : 0;  // first query tile with a visible key
   const int n_qt = (N + kBwdTile - 1) / kBwdTile;
   const int n_steps = a.group * (n_qt - t0);  // (query head, query tile) pairs, in that order
-  BwdStage<D, T> stq, sto;
+  // Step s (a query head and 64-query tile) sits in stage s % 2; step s+1's Q and dO tiles go
+  // straight from memory into the other stage while step s is computed, its L and D through one
+  // register of the first 128 threads; one barrier per step.
+  constexpr int W = kBwdKvWaves;
   float lsd = 0.f;
-  auto load_step = [&](int s) {
+  auto issue_step = [&](int s) {
     const int g = s / (n_qt - t0), t = t0 + s % (n_qt - t0);
     const int bh = b * a.H + hk * a.group + g;
     const long long qhead = b * a.q_bs + (long long)(hk * a.group + g) * a.q_hs;
-    bwd_load<D, T>(reinterpret_cast<const char*>(a.q + qhead), rs, t * kBwdTile, N, tid, stq);
-    bwd_load<D, T>(reinterpret_cast<const char*>(a.dout + qhead), rs, t * kBwdTile, N, tid, sto);
+    dma_tile<D, W>(sQ2[s & 1], reinterpret_cast<const char*>(a.q + qhead), rs, t * kBwdTile, N,
+                   wave, lane);
+    dma_tile<D, W>(sO2[s & 1], reinterpret_cast<const char*>(a.dout + qhead), rs, t * kBwdTile,
+                   N, wave, lane);
     if (tid < 2 * kBwdTile) {
       const int r = t * kBwdTile + (tid & (kBwdTile - 1));
       const long long idx = (long long)bh * N + min(r, N - 1);
       lsd = tid < kBwdTile ? a.lse[idx] * kLog2e : a.dsum[idx];
     }
   };
-  load_step(0);
+  auto publish_step = [&](int s) {  // after the DMA and the L/D loads of step s have landed
+    if (tid < kBwdTile) sL2[s & 1][tid] = lsd;
+    else if (tid < 2 * kBwdTile) sD2[s & 1][tid - kBwdTile] = lsd;
+  };
+  issue_step(0);
+  wait_dma();
+  publish_step(0);
+  __syncthreads();
   for (int s = 0; s < n_steps; s++) {
     const int t = t0 + s % (n_qt - t0);
-    if (s > 0) __syncthreads();
-    bwd_store<D, T>(sQ, tid, stq);
-    bwd_store<D, T>(sO, tid, sto);
-    if (tid < kBwdTile) sL[tid] = lsd;
-    else if (tid < 2 * kBwdTile) sD[tid - kBwdTile] = lsd;
-    __syncthreads();
-    if (s + 1 < n_steps) load_step(s + 1);
+    if (s + 1 < n_steps) issue_step(s + 1);
+    const char* sQ = sQ2[s & 1];
+    const char* sO = sO2[s & 1];
+    const float* sL = sL2[s & 1];
+    const float* sD = sD2[s & 1];
 #pragma unroll 1
     for (int sb = 0; sb < 2; sb++) {
       const int q0 = t * kBwdTile + 32 * sb;
@@ -380,6 +409,11 @@ __global__ __launch_bounds__(kBwdKvWaves * 64) __attribute__((amdgpu_waves_per_e
         for (int db = 0; db < DB; db++)
           acck[db] = __builtin_amdgcn_mfma_f32_32x32x16_bf16(bwd_tr<D>(sQ, 32 * sb + 16 * ks, db, lane),
                                                              dsf[ks], acck[db], 0, 0, 0);
+    }
+    if (s + 1 < n_steps) {
+      wait_dma();
+      publish_step(s + 1);
+      __syncthreads();
     }
   }
 
