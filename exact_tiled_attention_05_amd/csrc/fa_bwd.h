@@ -163,7 +163,8 @@ __global__ __launch_bounds__(kBwdQWaves * 64) __attribute__((amdgpu_waves_per_eu
   __shared__ __attribute__((aligned(1024))) char sK2[2][S::BYTES];  // two stages of K and V tiles
   __shared__ __attribute__((aligned(1024))) char sV2[2][S::BYTES];
 
-  const int tid = threadIdx.x, wave = tid >> 6, lane = tid & 63;
+  const int tid = threadIdx.x, lane = tid & 63;
+  const int wave = __builtin_amdgcn_readfirstlane(tid >> 6);  // uniform: keeps wave tests scalar
   const int c = lane & 31, h = lane >> 5;
   int bh, qblk;
   map_block<CAUSAL>(blockIdx.x, gridDim.x, a.BH, a.n_qblk, bh, qblk);
@@ -234,16 +235,15 @@ __global__ __launch_bounds__(kBwdQWaves * 64) __attribute__((amdgpu_waves_per_eu
 #pragma unroll
       for (int dk = 0; dk < DK; dk++)
         dpt = __builtin_amdgcn_mfma_f32_32x32x16_bf16(bwd_row<D>(sV, 32 * sb + c, dk, h), df[dk], dpt, 0, 0, 0);
-      // P^T = exp(S^T scale - L), masked; dS^T = P^T (dP^T - D)
-      const bool edge = (CAUSAL && k0 + 31 > qw0) || k0 + 31 >= N;
+      // P^T = exp(S^T scale - L), masked; dS^T = P^T (dP^T - D). Register i holds key
+      // k0 + acc_row(i, h), visible iff acc_row(i, 0) <= lim (keys below N and, causal, <= qrow).
+      const bool edge = (CAUSAL && k0 + 31 > qw0) || k0 + 31 >= N;  // wave-uniform
+      const int lim = (CAUSAL ? min(qrow, N - 1) : N - 1) - k0 - 4 * h;
       bf16x8 dsf[2];
 #pragma unroll
       for (int i = 0; i < 16; i++) {
         float p = fast_exp2(__builtin_fmaf(st[i], a.scale_log2, -lse2));
-        if (edge) {
-          const int key = k0 + acc_row(i, h);
-          if (key >= N || (CAUSAL && key > qrow)) p = 0.f;
-        }
+        if (edge) p = acc_row(i, 0) <= lim ? p : 0.f;
         dsf[i >> 3][i & 7] = (bf16)(p * (dpt[i] - drow));
       }
 #pragma unroll
@@ -286,7 +286,8 @@ __global__ __launch_bounds__(kBwdKvWaves * 64) __attribute__((amdgpu_waves_per_e
   __shared__ __attribute__((aligned(16))) float sD2[2][kBwdTile];    // D
   __shared__ __attribute__((aligned(1024))) char sVb[kBwdKvRows * S::ROW];  // this block's V rows
 
-  const int tid = threadIdx.x, wave = tid >> 6, lane = tid & 63;
+  const int tid = threadIdx.x, lane = tid & 63;
+  const int wave = __builtin_amdgcn_readfirstlane(tid >> 6);  // uniform: keeps wave tests scalar
   const int c = lane & 31, h = lane >> 5;
   int bkv, x;
   map_block<CAUSAL>(blockIdx.x, gridDim.x, a.BHkv, a.n_kblk, bkv, x);
@@ -357,7 +358,11 @@ __global__ __launch_bounds__(kBwdKvWaves * 64) __attribute__((amdgpu_waves_per_e
     for (int sb = 0; sb < 2; sb++) {
       const int q0 = t * kBwdTile + 32 * sb;
       if (q0 >= N || (CAUSAL && q0 + 31 < kw0)) continue;
-      const bool edge = (CAUSAL && q0 < kw0 + 31) || q0 + 31 >= N;
+      // register i holds query q0 + acc_row(i, h): visible iff below N and (causal) >= krow, i.e.
+      // lo <= acc_row(i, 0) <= hi
+      const bool edge = (CAUSAL && q0 < kw0 + 31) || q0 + 31 >= N;  // wave-uniform
+      const int hi = N - 1 - q0 - 4 * h;
+      const int lo = CAUSAL ? krow - q0 - 4 * h : -1024;
       // S = Q K^T, then P (rows: queries 32 sb + acc_row(i, h); L of those from LDS) and its
       // bf16 copy, then dV^T += dO^T P -- so S and the bf16 P are dead before dP is formed.
       f32x16 sc = f32x16{};
@@ -373,10 +378,7 @@ __global__ __launch_bounds__(kBwdKvWaves * 64) __attribute__((amdgpu_waves_per_e
         for (int e = 0; e < 4; e++) {
           const int i = 4 * j4 + e;
           float pi = fast_exp2(__builtin_fmaf(sc[i], a.scale_log2, -lv[e]));
-          if (edge) {
-            const int qi = q0 + acc_row(i, h);
-            if (qi >= N || (CAUSAL && krow > qi)) pi = 0.f;
-          }
+          if (edge) pi = (acc_row(i, 0) >= lo && acc_row(i, 0) <= hi) ? pi : 0.f;
           p[i] = pi;
           pf[i >> 3][i & 7] = (bf16)pi;
         }
