@@ -354,7 +354,7 @@ __global__ __launch_bounds__(kBwdKvWaves * 64) __attribute__((amdgpu_waves_per_e
     const char* sO = sO2[s & 1];
     const float* sL = sL2[s & 1];
     const float* sD = sD2[s & 1];
-#pragma unroll 1
+#pragma unroll
     for (int sb = 0; sb < 2; sb++) {
       const int q0 = t * kBwdTile + 32 * sb;
       if (q0 >= N || (CAUSAL && q0 + 31 < kw0)) continue;
