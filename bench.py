@@ -199,7 +199,7 @@ def bench_backward(args, w):
     qd, kd, vd, dod = (W.to_layout(x, layout).to(dev) for x in (q, k, v, do))
     o, lse = fa.forward(qd, kd, vd, scale=scale, causal=causal, layout=layout)
     dq, dk, dv = torch.empty_like(qd), torch.empty_like(kd), torch.empty_like(vd)
-    need = fa.fa_bwd_workspace_bytes(B, H, N)
+    need = fa.fa_bwd_workspace_bytes(B, H, H_kv, N, d)
     ws = torch.empty(need, dtype=torch.uint8, device=dev)
     stream = torch.cuda.current_stream(dev)
     argv = (qd.data_ptr(), kd.data_ptr(), vd.data_ptr(), o.data_ptr(), dod.data_ptr(),

@@ -14,7 +14,7 @@ Raw entry points (same names and argument order as the C-ABI; pointers are integ
     fa_splitkv_workspace_bytes(B, H, H_kv, N_q, N_kv, d, causal, n_splits) -> int
     fa_fwd_splitkv(q, k, v, o, lse, B, H, H_kv, N_q, N_kv, d, scale, causal, layout, n_splits,
                    workspace, workspace_bytes, stream) -> int
-    fa_bwd_workspace_bytes(B, H, N) -> int
+    fa_bwd_workspace_bytes(B, H, H_kv, N, d) -> int
     fa_bwd(q, k, v, o, dout, lse, dq, dk, dv, B, H, H_kv, N, d, scale, causal, layout, workspace,
            workspace_bytes, stream) -> int
     fa_strerror(code) -> str
@@ -83,7 +83,7 @@ def load_library():
                                        [ctypes.c_float] + [ctypes.c_int] * 3 +
                                        [ctypes.c_void_p, ctypes.c_size_t, ctypes.c_void_p])
         lib.fa_fwd_splitkv.restype = ctypes.c_int
-        lib.fa_bwd_workspace_bytes.argtypes = [ctypes.c_int] * 3
+        lib.fa_bwd_workspace_bytes.argtypes = [ctypes.c_int] * 5
         lib.fa_bwd_workspace_bytes.restype = ctypes.c_size_t
         lib.fa_bwd.argtypes = ([ctypes.c_void_p] * 9 + [ctypes.c_int] * 5 + [ctypes.c_float] +
                                [ctypes.c_int] * 2 + [ctypes.c_void_p, ctypes.c_size_t,
@@ -125,8 +125,8 @@ def fa_fwd_splitkv(q, k, v, o, lse, B, H, H_kv, N_q, N_kv, d, scale, causal, lay
                                          layout, n_splits, workspace, workspace_bytes, stream)
 
 
-def fa_bwd_workspace_bytes(B, H, N):
-    return load_library().fa_bwd_workspace_bytes(B, H, N)
+def fa_bwd_workspace_bytes(B, H, H_kv, N, d):
+    return load_library().fa_bwd_workspace_bytes(B, H, H_kv, N, d)
 
 
 def fa_bwd(q, k, v, o, dout, lse, dq, dk, dv, B, H, H_kv, N, d, scale, causal, layout, workspace,
@@ -259,8 +259,8 @@ def backward(q, k, v, o, lse, dout, scale=None, causal=False, layout="bhnd", dq=
     q, o, dout like forward()'s q and o; k, v its k and v; lse the float32 [B, H, N] logsumexp
     forward() returned for the same q, k, v, scale and mask. Returns (dq, dk, dv) shaped like q, k,
     v; for grouped K/V heads dk and dv hold the sums over each K/V head's query heads.
-    ``workspace`` (a uint8 tensor of at least fa_bwd_workspace_bytes(B, H, N) bytes) is allocated
-    here if not given.
+    ``workspace`` (a uint8 tensor of at least fa_bwd_workspace_bytes(B, H, H_kv, N, d) bytes) is
+    allocated here if not given.
     """
     import torch
 
@@ -290,7 +290,7 @@ def backward(q, k, v, o, lse, dout, scale=None, causal=False, layout="bhnd", dq=
     dq = torch.empty_like(q) if dq is None else dq
     dk = torch.empty_like(k) if dk is None else dk
     dv = torch.empty_like(v) if dv is None else dv
-    need = fa_bwd_workspace_bytes(B, H, N)
+    need = fa_bwd_workspace_bytes(B, H, H_kv, N, d)
     if workspace is None:
         workspace = torch.empty(max(need, 1), dtype=torch.uint8, device=q.device)
     if stream is None:

@@ -188,7 +188,24 @@ hipError_t launch_decode(fa::DecodeArgs a, hipStream_t s) {
 
 // ---- backward ----------------------------------------------------------------------------------
 
-size_t bwd_ws_bytes(int B, int H, int N) { return (size_t)B * H * N * sizeof(float); }
+// Query-head splits of the dK/dV kernel: enough (K/V head, key block, split) workgroups for about
+// four per CU, a divisor of the group size. MHA, and grouped heads with many K/V heads or long
+// sequences, need none; the Llama-3-8B layer (8 K/V heads, 32 key blocks) takes 4.
+int bwd_hsplit(int B, int H, int H_kv, int N) {
+  const int group = H / H_kv;
+  const int n_kblk = (N + fa::kBwdKvRows - 1) / fa::kBwdKvRows;
+  const int64_t wgs = (int64_t)n_kblk * B * H_kv;
+  int want = (int)std::min<int64_t>(group, (1024 + wgs - 1) / wgs);
+  while (group % want) want--;
+  return std::max(want, 1);
+}
+size_t bwd_dsum_bytes(int B, int H, int N) {
+  return ((size_t)B * H * N * sizeof(float) + 255) / 256 * 256;
+}
+size_t bwd_ws_bytes(int B, int H, int H_kv, int N, int d) {
+  const int hs = bwd_hsplit(B, H, H_kv, N);
+  return bwd_dsum_bytes(B, H, N) + (hs > 1 ? 2 * (size_t)hs * B * H_kv * N * d * sizeof(float) : 0);
+}
 
 template <int D, bool CAUSAL>
 hipError_t launch_bwd(fa::BwdArgs a, hipStream_t s) {
@@ -196,17 +213,22 @@ hipError_t launch_bwd(fa::BwdArgs a, hipStream_t s) {
   hipError_t e = hipLaunchKernel(reinterpret_cast<const void*>(&fa::fa_bwd_dq_kernel<D, CAUSAL>),
                                  dim3(a.n_qblk * a.BH), dim3(fa::kBwdQWaves * 64), args, 0, s);
   if (e != hipSuccess) return e;
-  return hipLaunchKernel(reinterpret_cast<const void*>(&fa::fa_bwd_dkdv_kernel<D, CAUSAL>),
-                         dim3(a.n_kblk * a.BHkv), dim3(fa::kBwdKvWaves * 64), args, 0, s);
+  e = hipLaunchKernel(reinterpret_cast<const void*>(&fa::fa_bwd_dkdv_kernel<D, CAUSAL>),
+                      dim3(a.n_kblk * a.BHkv * a.hsplit), dim3(fa::kBwdKvWaves * 64), args, 0, s);
+  if (e != hipSuccess || a.hsplit == 1) return e;
+  const long long n4 = (long long)a.BHkv * a.N * (D / 4);
+  return hipLaunchKernel(reinterpret_cast<const void*>(&fa::fa_bwd_combine_kernel<D>),
+                         dim3((unsigned)((n4 + 255) / 256)), dim3(256), args, 0, s);
 }
 
 }  // namespace
 
 extern "C" {
 
-size_t fa_bwd_workspace_bytes(int B, int H, int N) {
+size_t fa_bwd_workspace_bytes(int B, int H, int H_kv, int N, int d) {
   if (B < 1 || H < 1 || N < 1 || N > kMaxN || (int64_t)B * H > kMaxBH) return 0;
-  return bwd_ws_bytes(B, H, N);
+  if (H_kv < 1 || H_kv > H || H % H_kv != 0 || (d != 64 && d != 128)) return 0;
+  return bwd_ws_bytes(B, H, H_kv, N, d);
 }
 
 int fa_bwd(const void* q, const void* k, const void* v, const void* o, const void* dout,
@@ -220,7 +242,7 @@ int fa_bwd(const void* q, const void* k, const void* v, const void* o, const voi
                         reinterpret_cast<uintptr_t>(dk) | reinterpret_cast<uintptr_t>(dv) |
                         reinterpret_cast<uintptr_t>(workspace);
   if (mis & 15) return FA_ERR_ALIGNMENT;
-  const size_t wb = bwd_ws_bytes(B, H, N);
+  const size_t wb = bwd_ws_bytes(B, H, H_kv, N, d);
   if (workspace_bytes < wb) return FA_ERR_INVALID_ARG;
   const size_t qb = (size_t)B * H * N * d * 2, kb = (size_t)B * H_kv * N * d * 2;
   const size_t lb = (size_t)B * H * N * sizeof(float);
@@ -246,6 +268,8 @@ int fa_bwd(const void* q, const void* k, const void* v, const void* o, const voi
   a.dk = static_cast<fa::bf16*>(dk);
   a.dv = static_cast<fa::bf16*>(dv);
   a.dsum = static_cast<float*>(workspace);
+  a.hsplit = bwd_hsplit(B, H, H_kv, N);
+  a.part = reinterpret_cast<float*>(static_cast<char*>(workspace) + bwd_dsum_bytes(B, H, N));
   a.N = N;
   a.H = H;
   a.Hkv = H_kv;

@@ -21,7 +21,10 @@
 //     head that shares the K/V head, so grouped heads receive the sum of their query heads'
 //     gradients -- with Q, dO, L and D of each 64-query tile in LDS: S = Q K^T, dP = dO V^T
 //     (queries on M, keys on N), P and dS in fp32, then dV^T += dO^T P and dK^T += Q^T dS with
-//     P, dS rounded to bf16 and dO^T, Q^T read with the transposing LDS read.
+//     P, dS rounded to bf16 and dO^T, Q^T read with the transposing LDS read. When there are too
+//     few (K/V head, key block) pairs to fill the GPU (grouped heads), the query heads of a group
+//     are split over hsplit workgroups that write fp32 partial sums, and fa_bwd_combine_kernel
+//     adds them in split order (still deterministic).
 //
 // LDS layout of a 64-row tile: unpadded rows of 2d bytes; the 16-byte chunk j of row r is stored
 // at chunk position j ^ f(r). Tiles here are read both ways -- as rows (16 bytes of one row per
@@ -54,6 +57,8 @@ struct BwdArgs {
   bf16* dk;
   bf16* dv;
   float* dsum;  // D, [B * H][N] fp32 (written by the dQ kernel, read by the dK/dV kernel)
+  float* part;  // with hsplit > 1: fp32 partial dK then dV, each [hsplit][B * H_kv][N][d]
+  int hsplit;   // workgroups sharing one (K/V head, key block), each over group / hsplit query heads
   int N, H, Hkv, group;
   int BH, BHkv;  // B * H, B * H_kv
   int n_qblk, n_kblk;
@@ -289,10 +294,12 @@ __global__ __launch_bounds__(kBwdKvWaves * 64) __attribute__((amdgpu_waves_per_e
   const int tid = threadIdx.x, lane = tid & 63;
   const int wave = __builtin_amdgcn_readfirstlane(tid >> 6);  // uniform: keeps wave tests scalar
   const int c = lane & 31, h = lane >> 5;
-  int bkv, x;
-  map_block<CAUSAL>(blockIdx.x, gridDim.x, a.BHkv, a.n_kblk, bkv, x);
+  int vh, x;  // vh: (batch * K/V head, query-head split)
+  map_block<CAUSAL>(blockIdx.x, gridDim.x, a.BHkv * a.hsplit, a.n_kblk, vh, x);
   const int kblk = CAUSAL ? a.n_kblk - 1 - x : x;  // causal: the first key blocks, which see the
                                                    // most queries, first
+  const int bkv = vh / a.hsplit, split = vh - bkv * a.hsplit;
+  const int gps = a.group / a.hsplit, g0 = split * gps;  // this workgroup's query heads g0..
   const int b = bkv / a.Hkv, hk = bkv - b * a.Hkv;
   const int N = a.N;
   const int kw0 = kblk * kBwdKvRows + 32 * wave;
@@ -319,14 +326,14 @@ __global__ __launch_bounds__(kBwdKvWaves * 64) __attribute__((amdgpu_waves_per_e
 
   const int t0 = CAUSAL ? (kblk * kBwdKvRows) / kBwdTile : 0;  // first query tile with a visible key
   const int n_qt = (N + kBwdTile - 1) / kBwdTile;
-  const int n_steps = a.group * (n_qt - t0);  // (query head, query tile) pairs, in that order
+  const int n_steps = gps * (n_qt - t0);  // (query head, query tile) pairs, in that order
   // Step s (a query head and 64-query tile) sits in stage s % 2; step s+1's Q and dO tiles go
   // straight from memory into the other stage while step s is computed, its L and D through one
   // register of the first 128 threads; one barrier per step.
   constexpr int W = kBwdKvWaves;
   float lsd = 0.f;
   auto issue_step = [&](int s) {
-    const int g = s / (n_qt - t0), t = t0 + s % (n_qt - t0);
+    const int g = g0 + s / (n_qt - t0), t = t0 + s % (n_qt - t0);
     const int bh = b * a.H + hk * a.group + g;
     const long long qhead = b * a.q_bs + (long long)(hk * a.group + g) * a.q_hs;
     dma_tile<D, W>(sQ2[s & 1], reinterpret_cast<const char*>(a.q + qhead), rs, t * kBwdTile, N,
@@ -419,7 +426,24 @@ __global__ __launch_bounds__(kBwdKvWaves * 64) __attribute__((amdgpu_waves_per_e
     }
   }
 
-  if (krow < N) {
+  if (krow < N && a.hsplit > 1) {
+    // partial sums of this split, fp32; fa_bwd_combine_kernel adds the splits in order
+    const long long prow = ((long long)(split * a.BHkv + bkv) * N + krow) * D;
+    const long long pstride = (long long)a.hsplit * a.BHkv * N * D;  // dK part -> dV part
+#pragma unroll
+    for (int db = 0; db < DB; db++)
+#pragma unroll
+      for (int g4 = 0; g4 < 4; g4++) {
+        f32x4v k4, v4;
+#pragma unroll
+        for (int e = 0; e < 4; e++) {
+          k4[e] = acck[db][4 * g4 + e] * a.scale;
+          v4[e] = accv[db][4 * g4 + e];
+        }
+        *reinterpret_cast<f32x4v*>(a.part + prow + 32 * db + 8 * g4 + 4 * h) = k4;
+        *reinterpret_cast<f32x4v*>(a.part + pstride + prow + 32 * db + 8 * g4 + 4 * h) = v4;
+      }
+  } else if (krow < N) {
     bf16* dkr = a.dk + kvoff;
     bf16* dvr = a.dv + kvoff;
 #pragma unroll
@@ -436,6 +460,36 @@ __global__ __launch_bounds__(kBwdKvWaves * 64) __attribute__((amdgpu_waves_per_e
         *reinterpret_cast<bf16x4*>(dvr + 32 * db + 8 * g4 + 4 * h) = v4;
       }
   }
+}
+
+// dK, dV = sum over the hsplit partials, in split order, rounded to bf16 once. One thread per 4
+// consecutive elements of one K/V row.
+template <int D>
+__global__ __launch_bounds__(256) void fa_bwd_combine_kernel(BwdArgs a) {
+  const long long n4 = (long long)a.BHkv * a.N * (D / 4);
+  const long long i = (long long)blockIdx.x * 256 + threadIdx.x;
+  if (i >= n4) return;
+  const long long e = 4 * i;                  // element index in [B * H_kv][N][D]
+  const int col = (int)(e % D);
+  const long long row = e / D;                // (bkv, n)
+  const int n = (int)(row % a.N), bkv = (int)(row / a.N);
+  const int b = bkv / a.Hkv, hk = bkv - b * a.Hkv;
+  const long long pstride = (long long)a.hsplit * a.BHkv * a.N * D, sstride = (long long)a.BHkv * a.N * D;
+  f32x4v sk = *reinterpret_cast<const f32x4v*>(a.part + e);
+  f32x4v sv = *reinterpret_cast<const f32x4v*>(a.part + pstride + e);
+  for (int sp = 1; sp < a.hsplit; sp++) {
+    sk += *reinterpret_cast<const f32x4v*>(a.part + sp * sstride + e);
+    sv += *reinterpret_cast<const f32x4v*>(a.part + pstride + sp * sstride + e);
+  }
+  const long long off = b * a.kv_bs + hk * a.kv_hs + (long long)n * a.kv_rs + col;
+  bf16x4 k4, v4;
+#pragma unroll
+  for (int j = 0; j < 4; j++) {
+    k4[j] = (bf16)sk[j];
+    v4[j] = (bf16)sv[j];
+  }
+  *reinterpret_cast<bf16x4*>(a.dk + off) = k4;
+  *reinterpret_cast<bf16x4*>(a.dv + off) = v4;
 }
 
 }  // namespace fa

@@ -140,17 +140,19 @@ int fa_fwd_splitkv(const void* q, const void* k, const void* v, void* o, float* 
  * With grouped K/V heads (H_kv < H) a K/V head's dk and dv are the sums over the query heads
  * that use it (query head h uses K/V head h / (H / H_kv)).
  *
- * fa_bwd_workspace_bytes -- bytes of device workspace fa_bwd needs: B * H * N floats (D). Returns
- *   0 for an invalid shape.
+ * fa_bwd_workspace_bytes -- bytes of device workspace fa_bwd needs: B * H * N floats (D), and,
+ *   when the query heads of a K/V head are split over several workgroups to fill the GPU (grouped
+ *   heads with few K/V heads), fp32 partial dK and dV of every split. Returns 0 for an invalid
+ *   shape.
  * fa_bwd -- bf16 q, k, v, o, dout, dq, dk, dv in `layout` (q, o, dout, dq: H heads; k, v, dk, dv:
  *   H_kv heads; shapes as fa_fwd_gqa); fp32 lse [B][H][N]; fp32 arithmetic with the probabilities
  *   and dS rounded to bf16 as matrix-core operands. `workspace`: caller-owned device memory of at
  *   least fa_bwd_workspace_bytes(B, H, N) bytes, contents on entry irrelevant. Outputs must not
- *   overlap any input, each other or the workspace; all pointers 16-byte aligned. Two kernels are
- *   enqueued on `stream`; calls that share a workspace must not overlap. The result is
+ *   overlap any input, each other or the workspace; all pointers 16-byte aligned. Two or three
+ *   kernels are enqueued on `stream`; calls that share a workspace must not overlap. The result is
  *   deterministic (no atomics). Limits and return codes as fa_fwd_gqa (d in {64, 128}).
  */
-size_t fa_bwd_workspace_bytes(int B, int H, int N);
+size_t fa_bwd_workspace_bytes(int B, int H, int H_kv, int N, int d);
 int fa_bwd(const void* q, const void* k, const void* v, const void* o, const void* dout,
            const float* lse, void* dq, void* dk, void* dv, int B, int H, int H_kv, int N, int d,
            float scale, int causal, int layout, void* workspace, size_t workspace_bytes,

@@ -227,7 +227,7 @@ BAD_BWD = [
     (dict(do=0), fa.FA_ERR_INVALID_ARG),
     (dict(dk=0), fa.FA_ERR_INVALID_ARG),
     (dict(o=0), fa.FA_ERR_INVALID_ARG),
-    (dict(ws_bytes=2 * 8 * 300 * 4 - 1), fa.FA_ERR_INVALID_ARG),  # one byte short of B*H*N floats
+    (dict(ws_bytes=2 * 8 * 300 * 4 - 1), fa.FA_ERR_INVALID_ARG),  # short of even the D part
     (dict(N=0), fa.FA_ERR_INVALID_ARG),
     (dict(H_kv=3), fa.FA_ERR_INVALID_ARG),
     (dict(layout=2), fa.FA_ERR_INVALID_ARG),
@@ -249,9 +249,18 @@ def test_bad_backward_arguments_are_refused(kw, code):
 
 
 def test_backward_workspace_bytes():
-    assert fa.fa_bwd_workspace_bytes(2, 8, 300) == 2 * 8 * 300 * 4
-    assert fa.fa_bwd_workspace_bytes(0, 8, 300) == 0
-    assert fa.fa_bwd_workspace_bytes(1, 1, (1 << 22) + 1) == 0
+    f = fa.fa_bwd_workspace_bytes
+    # D (B*H*N floats, 256-byte aligned) only, when no query-head split is needed (MHA)
+    assert f(2, 8, 8, 300, 128) == 2 * 8 * 300 * 4
+    # Llama-3-8B grouped layer: 32 key blocks x 8 K/V heads = 256 workgroups -> 4 splits, each
+    # with fp32 partial dK and dV
+    assert f(1, 32, 8, 8192, 128) == 32 * 8192 * 4 + 2 * 4 * 8 * 8192 * 128 * 4
+    # few workgroups: the split is the largest divisor of the group size up to the need
+    assert f(2, 8, 2, 300, 128) == 19200 + 2 * 4 * 2 * 2 * 300 * 128 * 4
+    assert f(0, 8, 8, 300, 128) == 0
+    assert f(1, 1, 1, (1 << 22) + 1, 128) == 0
+    assert f(1, 8, 3, 300, 128) == 0
+    assert f(1, 8, 8, 300, 96) == 0
 
 
 def test_backward_binding_checks_tensors_before_calling():

@@ -178,7 +178,7 @@ def test_backward_scale_zero():
 def test_backward_deterministic_and_workspace_reuse():
     q, k, v = make_inputs(2, 8, 1000, 128, H_kv=2, seed=21)
     do = make_inputs(2, 8, 1000, 128, seed=22)[0]
-    ws = torch.empty(fa.fa_bwd_workspace_bytes(2, 8, 1000), dtype=torch.uint8, device=DEV)
+    ws = torch.empty(fa.fa_bwd_workspace_bytes(2, 8, 2, 1000, 128), dtype=torch.uint8, device=DEV)
     a = gpu_fwd_bwd(q, k, v, do, 0.1, True, "bnhd", workspace=ws)
     small = make_inputs(1, 2, 77, 64, seed=23)
     gpu_fwd_bwd(*small, make_inputs(1, 2, 77, 64, seed=24)[0], 0.1, False, workspace=ws)
