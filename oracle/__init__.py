@@ -8,8 +8,9 @@ Contents
 --------
 attention.py  -- the plain definition: materialise S = scale * Q K^T, mask, stable softmax,
                  O = P V and LSE = m + ln(l), in float64, one (batch, head) at a time; and the
-                 grouped-K/V-head form (each query head with its assigned K/V head), and the
-                 decoding form (N_q queries that are the last N_q of N_kv tokens).
+                 grouped-K/V-head form (each query head with its assigned K/V head), the
+                 decoding form (N_q queries that are the last N_q of N_kv tokens), and the score
+                 modifiers (sliding window, ALiBi, additive bias) of attention_ext.
 backward.py   -- the gradients of the plain definition (dQ, dK, dV from dO), dense, in float64,
                  per head and with grouped K/V heads.
 online.py     -- the pages' streaming recurrences (online normaliser, blockwise (m, l, a)
@@ -20,7 +21,7 @@ Every function is pinned by ``tests/test_oracle*.py`` and ``tests/test_online_mo
 something other than itself: the worked example printed on the pages, closed forms,
 invariants, brute force in scalar Python, and float64 library routines.
 """
-from .attention import (attention, attention_decode, attention_gqa, attention_head,  # noqa: F401
-                        dense_scores, kv_head_of)
+from .attention import (attention, attention_decode, attention_ext, attention_gqa,  # noqa: F401
+                        attention_head, dense_scores, kv_head_of)
 from .backward import attention_backward, attention_backward_head  # noqa: F401
 from .online import online_normalizer, blockwise_row, tiled_attention  # noqa: F401

@@ -28,28 +28,49 @@ Readings where the pages leave a choice open:
 import numpy as np
 
 
-def dense_scores(q, k, scale, causal, rows, query_offset=0):
-    """S = scale * q[rows] k^T with the causal rule applied (future keys -> -inf).
+def dense_scores(q, k, scale, causal, rows, query_offset=0, window=None, alibi_slope=None,
+                 bias=None):
+    """S = scale * q[rows] k^T (+ bias) with the masks applied (hidden keys -> -inf).
 
     q: [Nq, d], k: [N, d] float64; rows: int array of query indices into q. Query row i is token
     i + query_offset of the sequence (0 for self-attention over the same tokens), and the causal
     rule keeps keys j <= i + query_offset.
+    Optional score modifiers ("Understanding FlashAttention Pt 1", §0.2: S = QK^T / sqrt(d) + B,
+    B an additive mask or bias; §3.5 and §4.2: local/sliding-window attention and ALiBi-style
+    bias), with positions i = row + query_offset and j = key index:
+      window = (left, right): key j visible iff i - left <= j <= i + right (a negative bound is
+               unbounded); combined with the causal rule when causal is set;
+      alibi_slope = m: adds -m |i - j| to the scaled score;
+      bias: [Nq, N] array added to the scaled score (its rows indexed like q).
     Returns S: [len(rows), N] float64.
     """
+    rows = np.asarray(rows)
     s = float(scale) * (q[rows] @ k.T)
+    key_pos = np.arange(k.shape[0])[None, :]
+    qry_pos = rows[:, None] + int(query_offset)
+    if bias is not None:
+        s = s + np.asarray(bias, dtype=np.float64)[rows]
+    if alibi_slope is not None:
+        s = s - float(alibi_slope) * np.abs(qry_pos - key_pos)
+    visible = np.ones(s.shape, dtype=bool)
     if causal:
-        key_pos = np.arange(k.shape[0])[None, :]
-        qry_pos = np.asarray(rows)[:, None] + int(query_offset)
-        s = np.where(key_pos <= qry_pos, s, -np.inf)
-    return s
+        visible &= key_pos <= qry_pos
+    if window is not None:
+        left, right = window
+        if left >= 0:
+            visible &= key_pos >= qry_pos - left
+        if right >= 0:
+            visible &= key_pos <= qry_pos + right
+    return np.where(visible, s, -np.inf)
 
 
-def attention_head(q, k, v, scale, causal=False, rows=None, return_sp=False, query_offset=0):
+def attention_head(q, k, v, scale, causal=False, rows=None, return_sp=False, query_offset=0,
+                   window=None, alibi_slope=None, bias=None):
     """One head of naive attention in float64.
 
     q: [Nq, d], k: [N, d], v: [N, dv] (any float dtype; upcast to float64); Nq = N for
-       self-attention. query_offset: position of query row 0 in the key sequence (see
-       dense_scores).
+       self-attention. query_offset: position of query row 0 in the key sequence; window,
+       alibi_slope, bias: optional score modifiers (see dense_scores).
     rows: optional sequence of query indices to evaluate (default: all Nq rows). Only those
           rows of S are formed, each against every key.
     Returns (O [R, dv], LSE [R]) and, if return_sp, also (S [R, N], P [R, N]).
@@ -60,7 +81,7 @@ def attention_head(q, k, v, scale, causal=False, rows=None, return_sp=False, que
     if rows is None:
         rows = np.arange(q.shape[0])
     rows = np.asarray(rows, dtype=np.int64)
-    s = dense_scores(q, k, scale, causal, rows, query_offset)
+    s = dense_scores(q, k, scale, causal, rows, query_offset, window, alibi_slope, bias)
     m = s.max(axis=1)
     if not np.all(np.isfinite(m)):
         raise ValueError("a query row has no visible key; its softmax is undefined")
@@ -164,4 +185,38 @@ def attention_decode(q, k, v, scale, causal=False):
             j = kv_head_of(h, H, H_kv)
             o[b, h], lse[b, h] = attention_head(q[b, h], k[b, j], v[b, j], scale, causal,
                                                 query_offset=Nkv - Nq)
+    return o, lse
+
+
+def attention_ext(q, k, v, scale, causal=False, window=None, alibi_slopes=None, bias=None,
+                  rows=None):
+    """Batched attention with grouped K/V heads and the optional score modifiers of dense_scores.
+
+    q: [B, H, N, d]; k, v: [B, H_kv, N, d]; alibi_slopes: optional length-H sequence (one slope per
+    query head); bias: optional [Bb, Hb, N, N] array with Bb in {1, B} and Hb in {1, H} (size-1
+    dimensions are shared). rows as in attention(). Returns (O [B, H, R, dv], LSE [B, H, R]).
+    """
+    q = np.asarray(q)
+    k = np.asarray(k)
+    v = np.asarray(v)
+    B, H = q.shape[0], q.shape[1]
+    H_kv = k.shape[1]
+    R = q.shape[2] if rows is None else np.asarray(rows).shape[-1]
+    o = np.empty((B, H, R, v.shape[3]), dtype=np.float64)
+    lse = np.empty((B, H, R), dtype=np.float64)
+    for b in range(B):
+        for h in range(H):
+            j = kv_head_of(h, H, H_kv)
+            if rows is None:
+                r = None
+            else:
+                ra = np.asarray(rows)
+                r = ra if ra.ndim == 1 else ra[b, h]
+            bm = None
+            if bias is not None:
+                bb = np.asarray(bias)
+                bm = bb[b if bb.shape[0] > 1 else 0, h if bb.shape[1] > 1 else 0]
+            slope = None if alibi_slopes is None else float(alibi_slopes[h])
+            o[b, h], lse[b, h] = attention_head(q[b, h], k[b, j], v[b, j], scale, causal, r,
+                                                window=window, alibi_slope=slope, bias=bm)
     return o, lse
