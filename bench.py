@@ -178,6 +178,102 @@ def bench_decode(args, w):
     print(json.dumps(rec), flush=True)
 
 
+def bench_variant(args, w):
+    """Score-variant workloads (sliding window, ALiBi, additive bias): one step = one fa_fwd_ext
+    call. Reported in TFLOP/s of the visible (query, key) pairs, 4*d FLOPs each."""
+    import numpy as np
+    import torch
+    import exact_tiled_attention_05_amd as fa
+    from exact_tiled_attention_05_amd import workloads as W
+    from oracle import attention_head
+
+    causal = w["causal"][-1]
+    q, k, v, scale = W.workload_inputs(args.workload)
+    B, H, N, d = w["B"], w["H"], w["N"], w["d"]
+    H_kv = w.get("H_kv", H)
+    layout = w.get("layout", "bhnd")
+    lay = fa.FA_LAYOUT_BHND if layout == "bhnd" else fa.FA_LAYOUT_BNHD
+    window = w.get("window", (-1, -1))
+    dev = torch.device("cuda:0")
+    qd, kd, vd = (W.to_layout(x, layout).to(dev) for x in (q, k, v))
+    o = torch.empty_like(qd)
+    lse = torch.empty((B, H, N), dtype=torch.float32, device=dev)
+    slopes = W.alibi_slopes(H).to(dev) if w.get("alibi") else None
+    bias = W.workload_bias(args.workload).to(dev) if w.get("bias_seed") else None
+    stream = torch.cuda.current_stream(dev)
+    argv = (qd.data_ptr(), kd.data_ptr(), vd.data_ptr(), o.data_ptr(), lse.data_ptr(), B, H, H_kv,
+            N, d, scale, int(causal), lay, window[0], window[1],
+            slopes.data_ptr() if slopes is not None else None,
+            bias.data_ptr() if bias is not None else None, 0,
+            bias.stride(1) if bias is not None else 0, bias.stride(2) if bias is not None else 0,
+            stream.cuda_stream)
+
+    def step():
+        rc = fa.fa_fwd_ext(*argv)
+        if rc != fa.FA_OK:
+            raise fa.FAError(rc, "fa_fwd_ext")
+
+    for _ in range(args.warmup):
+        step()
+    torch.cuda.synchronize()
+    e0 = torch.cuda.Event(enable_timing=True)
+    e1 = torch.cuda.Event(enable_timing=True)
+    t0 = time.perf_counter()
+    e0.record(stream)
+    for _ in range(args.steps):
+        step()
+    e1.record(stream)
+    torch.cuda.synchronize()
+    wall = time.perf_counter() - t0
+    ms = e0.elapsed_time(e1) / args.steps
+    win = None if tuple(window) == (-1, -1) else tuple(window)
+    flops = W.metric_flops_masked(B, H, N, d, causal, win)
+    tflops = flops / (ms * 1e-3) / 1e12
+    rec = {
+        "metric": "attention fwd TFLOP/s (4*d per visible query-key pair)",
+        "value": round(tflops, 2), "unit": "TFLOP/s", "n_gpus": 1, "steps": args.steps,
+        "warmup": args.warmup, "ms_per_step": round(ms, 5), "higher_is_better": True,
+        "scaling": "weak", "vs_baseline": None, "dtype": "bf16",
+        "data": "synthetic (seeded N(0,1) Q, K, V%s)" % (", bias" if bias is not None else ""),
+        "config": {"workload": args.workload, "B": B, "H": H, "H_kv": H_kv, "N": N, "d": d,
+                   "causal": causal, "layout": layout, "window": list(window),
+                   "alibi": bool(w.get("alibi")), "bias": bias is not None,
+                   "kernel": "fa_fwd_ext (fa_fwd_ext_kernel)"},
+        "roofline": {"bound": "mfma", "achieved": round(tflops, 2), "peak": PEAK_BF16_TFLOPS,
+                     "unit": "TFLOP/s", "frac": round(tflops / PEAK_BF16_TFLOPS, 4),
+                     "traffic": recorded_traffic(args.workload)},
+        "wall_s_timed_region": round(wall, 4),
+    }
+    if not args.no_cpu:
+        try:
+            from threadpoolctl import threadpool_info
+            threads = max([i.get("num_threads", 1) for i in threadpool_info()
+                           if i.get("user_api") == "blas"] or [1])
+        except Exception:  # pragma: no cover
+            threads = 1
+        group = H // H_kv
+        sl = W.alibi_slopes(H).tolist() if w.get("alibi") else None
+        bcpu = W.workload_bias(args.workload) if w.get("bias_seed") else None
+        dt, done = 0.0, 0
+        for h in range(H):
+            qh = q[0, h].float().numpy().astype(np.float64)
+            kh, vh = (x[0, h // group].float().numpy().astype(np.float64) for x in (k, v))
+            bm = bcpu[0, h].float().numpy().astype(np.float64) if bcpu is not None else None
+            t1 = time.perf_counter()
+            attention_head(qh, kh, vh, scale, causal, window=win,
+                           alibi_slope=None if sl is None else sl[h], bias=bm)
+            dt += time.perf_counter() - t1
+            done += 1
+            if dt >= 15.0:
+                break
+        cflops = W.metric_flops_masked(1, done, N, d, causal, win)
+        rec["cpu_baseline"] = {"value": cflops / dt / 1e12, "unit": "TFLOP/s", "cores": threads,
+                               "kind": "oracle",
+                               "sample": "%d of %d heads of batch 0, every row (numpy float64, "
+                                         "dense S and P), %.1f s" % (done, B * H, dt)}
+    print(json.dumps(rec), flush=True)
+
+
 def bench_backward(args, w):
     """Backward workloads: one step = one fa_bwd call (the dQ kernel, then the dK/dV kernel), with
     O and the logsumexp from one forward call and the workspace allocated before the timed
@@ -317,6 +413,8 @@ def main():
         return bench_decode(args, w)
     if w.get("backward"):
         return bench_backward(args, w)
+    if w.get("window") or w.get("alibi") or w.get("bias_seed"):
+        return bench_variant(args, w)
     causal = w["causal"][-1]
     q, k, v, scale = W.workload_inputs(args.workload)
     layout = w.get("layout", "bhnd")

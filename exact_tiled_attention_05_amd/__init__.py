@@ -11,6 +11,9 @@ Raw entry points (same names and argument order as the C-ABI; pointers are integ
     fa_fwd_f32(q, k, v, o, lse, B, H, N, d, scale, causal, stream) -> int
     fa_fwd_gqa(q, k, v, o, lse, B, H, H_kv, N, d, scale, causal, layout, stream) -> int
     fa_fwd_gqa_f32(q, k, v, o, lse, B, H, H_kv, N, d, scale, causal, layout, stream) -> int
+    fa_fwd_ext(q, k, v, o, lse, B, H, H_kv, N, d, scale, causal, layout, window_left,
+               window_right, alibi_slopes, bias, bias_batch_stride, bias_head_stride,
+               bias_row_stride, stream) -> int
     fa_splitkv_workspace_bytes(B, H, H_kv, N_q, N_kv, d, causal, n_splits) -> int
     fa_fwd_splitkv(q, k, v, o, lse, B, H, H_kv, N_q, N_kv, d, scale, causal, layout, n_splits,
                    workspace, workspace_bytes, stream) -> int
@@ -22,6 +25,8 @@ Raw entry points (same names and argument order as the C-ABI; pointers are integ
 Tensor convenience (PyTorch supplies device memory and the stream):
     forward(q, k, v, scale=None, causal=False, out=None, lse=None, stream=None, layout="bhnd")
         -> (o, lse)
+    forward_ext(q, k, v, scale=None, causal=False, layout="bhnd", window=(-1, -1),
+                alibi_slopes=None, bias=None, out=None, lse=None, stream=None) -> (o, lse)
     decode(q, k, v, scale=None, causal=False, layout="bhnd", n_splits=0, out=None, lse=None,
            workspace=None, stream=None) -> (o, lse)
     backward(q, k, v, o, lse, dout, scale=None, causal=False, layout="bhnd", dq=None, dk=None,
@@ -31,7 +36,8 @@ import ctypes
 import math
 import os
 
-__all__ = ["fa_fwd", "fa_fwd_f32", "fa_fwd_gqa", "fa_fwd_gqa_f32", "fa_fwd_splitkv", "fa_bwd",
+__all__ = ["fa_fwd", "fa_fwd_f32", "fa_fwd_gqa", "fa_fwd_gqa_f32", "fa_fwd_ext", "forward_ext",
+           "fa_fwd_splitkv", "fa_bwd",
            "fa_bwd_workspace_bytes", "backward",
            "fa_splitkv_workspace_bytes", "fa_strerror", "fa_version", "forward", "decode", "FAError", "library_path", "load_library", "FA_OK", "FA_ERR_INVALID_ARG",
            "FA_ERR_UNSUPPORTED", "FA_ERR_ALIGNMENT", "FA_ERR_LAUNCH", "FA_LAYOUT_BHND",
@@ -77,6 +83,10 @@ def load_library():
             fn = getattr(lib, name)
             fn.argtypes = argt
             fn.restype = ctypes.c_int
+        lib.fa_fwd_ext.argtypes = ([ctypes.c_void_p] * 5 + [ctypes.c_int] * 5 + [ctypes.c_float] +
+                                   [ctypes.c_int] * 4 + [ctypes.c_void_p] * 2 +
+                                   [ctypes.c_longlong] * 3 + [ctypes.c_void_p])
+        lib.fa_fwd_ext.restype = ctypes.c_int
         lib.fa_splitkv_workspace_bytes.argtypes = [ctypes.c_int] * 8
         lib.fa_splitkv_workspace_bytes.restype = ctypes.c_size_t
         lib.fa_fwd_splitkv.argtypes = ([ctypes.c_void_p] * 5 + [ctypes.c_int] * 6 +
@@ -113,6 +123,14 @@ def fa_fwd_gqa(q, k, v, o, lse, B, H, H_kv, N, d, scale, causal, layout, stream=
 def fa_fwd_gqa_f32(q, k, v, o, lse, B, H, H_kv, N, d, scale, causal, layout, stream=None):
     return load_library().fa_fwd_gqa_f32(q, k, v, o, lse, B, H, H_kv, N, d, scale, causal,
                                          layout, stream)
+
+
+def fa_fwd_ext(q, k, v, o, lse, B, H, H_kv, N, d, scale, causal, layout, window_left,
+               window_right, alibi_slopes, bias, bias_batch_stride, bias_head_stride,
+               bias_row_stride, stream=None):
+    return load_library().fa_fwd_ext(q, k, v, o, lse, B, H, H_kv, N, d, scale, causal, layout,
+                                     window_left, window_right, alibi_slopes, bias,
+                                     bias_batch_stride, bias_head_stride, bias_row_stride, stream)
 
 
 def fa_splitkv_workspace_bytes(B, H, H_kv, N_q, N_kv, d, causal, n_splits):
@@ -303,3 +321,73 @@ def backward(q, k, v, o, lse, dout, scale=None, causal=False, layout="bhnd", dq=
     if rc != FA_OK:
         raise FAError(rc, "fa_bwd")
     return dq, dk, dv
+
+
+def forward_ext(q, k, v, scale=None, causal=False, layout="bhnd", window=(-1, -1),
+                alibi_slopes=None, bias=None, out=None, lse=None, stream=None):
+    """forward() with a sliding window, ALiBi slopes and/or an additive bias (bf16 tensors).
+
+    window: (left, right), key j visible to query i iff i - left <= j <= i + right (-1: that side
+    unbounded). alibi_slopes: float32 tensor [H] on q's device (score -= slope_h |i - j|). bias: bf16
+    tensor broadcastable to [B, H, N, N] (size-1 batch/head dimensions are shared), contiguous in
+    its last dimension, added to the scaled scores. Returns (o, lse) like forward().
+    """
+    import torch
+
+    if layout not in ("bhnd", "bnhd"):
+        raise ValueError("layout must be 'bhnd' or 'bnhd'")
+    if q.dim() != 4 or k.dim() != 4 or k.shape != v.shape:
+        raise ValueError("q, k, v must be 4-D and k, v must have the same shape")
+    if layout == "bhnd":
+        B, H, N, d = q.shape
+        Bk, H_kv, Nk, dk = k.shape
+    else:
+        B, N, H, d = q.shape
+        Bk, Nk, H_kv, dk = k.shape
+    if (Bk, Nk, dk) != (B, N, d) or H_kv < 1 or H % H_kv != 0:
+        raise ValueError("k, v must match q in batch, length and head dim, with H a multiple of "
+                         "their head count")
+    if not (q.dtype == k.dtype == v.dtype == torch.bfloat16):
+        raise ValueError("q, k, v must all be bfloat16")
+    if not (q.is_cuda and k.device == q.device and v.device == q.device):
+        raise ValueError("q, k, v must be on the same GPU device")
+    if not (q.is_contiguous() and k.is_contiguous() and v.is_contiguous()):
+        raise ValueError("q, k, v must be contiguous")
+    if scale is None:
+        scale = 1.0 / math.sqrt(d)
+    wl, wr = (int(window[0]), int(window[1]))
+    sp = 0
+    if alibi_slopes is not None:
+        if alibi_slopes.dtype != torch.float32 or alibi_slopes.numel() != H or \
+                alibi_slopes.device != q.device or not alibi_slopes.is_contiguous():
+            raise ValueError("alibi_slopes must be a contiguous float32 tensor of H values on "
+                             "q's device")
+        sp = alibi_slopes.data_ptr()
+    bp, bs, hs, rs = 0, 0, 0, 0
+    if bias is not None:
+        if bias.dtype != torch.bfloat16 or bias.dim() != 4 or bias.device != q.device:
+            raise ValueError("bias must be a 4-D bfloat16 tensor on q's device")
+        if bias.shape[0] not in (1, B) or bias.shape[1] not in (1, H) or \
+                tuple(bias.shape[2:]) != (N, N) or bias.stride(3) != 1:
+            raise ValueError("bias must broadcast to [B, H, N, N] and be contiguous in its last "
+                             "dimension")
+        if bias.stride(2) % 4 or bias.data_ptr() % 8:
+            raise ValueError("bias rows must start 8-byte aligned: a row stride that is a multiple "
+                             "of 4 elements (pad the last dimension)")
+        bp = bias.data_ptr()
+        bs = bias.stride(0) if bias.shape[0] > 1 else 0
+        hs = bias.stride(1) if bias.shape[1] > 1 else 0
+        rs = bias.stride(2)
+    if out is None:
+        out = torch.empty_like(q)
+    if lse is None:
+        lse = torch.empty((B, H, N), dtype=torch.float32, device=q.device)
+    if stream is None:
+        stream = torch.cuda.current_stream(q.device).cuda_stream
+    lay = FA_LAYOUT_BHND if layout == "bhnd" else FA_LAYOUT_BNHD
+    rc = fa_fwd_ext(q.data_ptr(), k.data_ptr(), v.data_ptr(), out.data_ptr(), lse.data_ptr(), B, H,
+                    H_kv, N, d, float(scale), int(bool(causal)), lay, wl, wr, sp or None,
+                    bp or None, bs, hs, rs, stream)
+    if rc != FA_OK:
+        raise FAError(rc, "fa_fwd_ext")
+    return out, lse

@@ -11,11 +11,12 @@
 #include "fa_bwd.h"
 #include "fa_decode.h"
 #include "fa_fwd_bf16.h"
+#include "fa_fwd_ext.h"
 #include "fa_fwd_f32.h"
 
 namespace {
 
-constexpr int kVersion = 400;  // 0.4.0: backward pass
+constexpr int kVersion = 500;  // 0.5.0: score variants (window, ALiBi, bias) and d = 256
 constexpr int kMaxN = 1 << 22;
 constexpr int kMaxBH = 65535;  // grid y of the fp32 kernel; also keeps bf16 grids < 2^31
 
@@ -24,10 +25,11 @@ bool ranges_overlap(const void* a, size_t na, const void* b, size_t nb) {
   return x < y + nb && y < x + na;
 }
 
-// Shared argument checks; elem is the byte size of one q/k/v/o element.
+// Shared argument checks; elem is the byte size of one q/k/v/o element; d256: whether d = 256 is
+// accepted (by the bf16 forward only).
 int check_args(const void* q, const void* k, const void* v, const void* o, const void* lse,
                int B, int H, int H_kv, int N, int d, float scale, int causal, int layout,
-               size_t elem) {
+               size_t elem, bool d256 = false) {
   if (!q || !k || !v || !o || !lse) return FA_ERR_INVALID_ARG;
   if (B < 1 || H < 1 || N < 1 || N > kMaxN) return FA_ERR_INVALID_ARG;
   if ((int64_t)B * H > kMaxBH) return FA_ERR_INVALID_ARG;
@@ -35,7 +37,7 @@ int check_args(const void* q, const void* k, const void* v, const void* o, const
   if (layout != FA_LAYOUT_BHND && layout != FA_LAYOUT_BNHD) return FA_ERR_INVALID_ARG;
   if (causal != 0 && causal != 1) return FA_ERR_INVALID_ARG;
   if (!std::isfinite(scale) || scale < 0.f) return FA_ERR_INVALID_ARG;
-  if (d != 64 && d != 128) return FA_ERR_UNSUPPORTED;
+  if (d != 64 && d != 128 && !(d256 && d == 256)) return FA_ERR_UNSUPPORTED;
   const uintptr_t mis = reinterpret_cast<uintptr_t>(q) | reinterpret_cast<uintptr_t>(k) |
                         reinterpret_cast<uintptr_t>(v) | reinterpret_cast<uintptr_t>(o) |
                         reinterpret_cast<uintptr_t>(lse);
@@ -90,8 +92,88 @@ hipError_t launch_f32(fa::F32Args a, int n_qblk, hipStream_t s) {
                          dim3(n_qblk, a.BH), dim3(fa::kF32BlockQ), args, 0, s);
 }
 
+// ---- score variants and d = 256 ------------------------------------------------------------------
+
+template <int D, bool CAUSAL, bool ALIBI, bool BIAS>
+hipError_t launch_ext_t(fa::ExtArgs a, hipStream_t s) {
+  void* args[] = {&a};
+  return hipLaunchKernel(reinterpret_cast<const void*>(&fa::fa_fwd_ext_kernel<D, CAUSAL, ALIBI, BIAS>),
+                         dim3(a.n_qblk * a.BH), dim3(fa::kExtWaves * 64), args, 0, s);
+}
+template <int D, bool CAUSAL>
+hipError_t launch_ext_c(fa::ExtArgs a, hipStream_t s) {
+  const bool al = a.slopes != nullptr, bi = a.bias != nullptr;
+  if (al) return bi ? launch_ext_t<D, CAUSAL, true, true>(a, s) : launch_ext_t<D, CAUSAL, true, false>(a, s);
+  return bi ? launch_ext_t<D, CAUSAL, false, true>(a, s) : launch_ext_t<D, CAUSAL, false, false>(a, s);
+}
+template <int D>
+hipError_t launch_ext_d(fa::ExtArgs a, int causal, hipStream_t s) {
+  return causal ? launch_ext_c<D, true>(a, s) : launch_ext_c<D, false>(a, s);
+}
+
+int run_ext(const void* q, const void* k, const void* v, void* o, float* lse, int B, int H,
+            int H_kv, int N, int d, float scale, int causal, int layout, int window_left,
+            int window_right, const float* slopes, const void* bias, long long bias_bs,
+            long long bias_hs, long long bias_rs, void* stream) {
+  const int rc = check_args(q, k, v, o, lse, B, H, H_kv, N, d, scale, causal, layout, 2, true);
+  if (rc != FA_OK) return rc;
+  if (window_left < -1 || window_right < -1) return FA_ERR_INVALID_ARG;
+  const size_t qb = (size_t)B * H * N * d * 2, lb = (size_t)B * H * N * sizeof(float);
+  if (slopes) {
+    if (reinterpret_cast<uintptr_t>(slopes) & 3) return FA_ERR_ALIGNMENT;
+    if (ranges_overlap(slopes, H * sizeof(float), o, qb) ||
+        ranges_overlap(slopes, H * sizeof(float), lse, lb))
+      return FA_ERR_INVALID_ARG;
+  }
+  if (bias) {
+    if (bias_bs < 0 || bias_hs < 0 || bias_rs < N) return FA_ERR_INVALID_ARG;
+    if ((reinterpret_cast<uintptr_t>(bias) & 7) || (bias_rs & 3)) return FA_ERR_ALIGNMENT;
+    // one head's matrix is addressed with 32-bit byte offsets
+    if (((int64_t)(N - 1) * bias_rs + N) * 2 >= ((int64_t)1 << 31)) return FA_ERR_UNSUPPORTED;
+    const size_t bb = (size_t)(((int64_t)(B - 1) * bias_bs + (int64_t)(H - 1) * bias_hs +
+                                (int64_t)(N - 1) * bias_rs + N) * 2);
+    if (ranges_overlap(bias, bb, o, qb) || ranges_overlap(bias, bb, lse, lb))
+      return FA_ERR_INVALID_ARG;
+  }
+  fa::ExtArgs a;
+  a.q = static_cast<const fa::bf16*>(q);
+  a.k = static_cast<const fa::bf16*>(k);
+  a.v = static_cast<const fa::bf16*>(v);
+  a.o = static_cast<fa::bf16*>(o);
+  a.lse = lse;
+  a.bias = static_cast<const fa::bf16*>(bias);
+  a.slopes = slopes;
+  a.bias_bs = bias_bs;
+  a.bias_hs = bias_hs;
+  a.bias_rs = (int)bias_rs;
+  a.N = N;
+  a.H = H;
+  a.Hkv = H_kv;
+  a.group = H / H_kv;
+  a.BH = B * H;
+  a.n_qblk = (N + fa::kExtRows - 1) / fa::kExtRows;
+  a.wl = window_left < 0 ? fa::kExtNoWindow : std::min(window_left, N);
+  a.wr = window_right < 0 ? fa::kExtNoWindow : std::min(window_right, N);
+  a.scale_log2 = scale * fa::kLog2e;
+  const Strides sq = strides_of(layout, H, N, d), sk = strides_of(layout, H_kv, N, d);
+  a.q_bs = sq.bs;
+  a.q_hs = sq.hs;
+  a.q_rs = sq.rs;
+  a.kv_bs = sk.bs;
+  a.kv_hs = sk.hs;
+  a.kv_rs = sk.rs;
+  const hipStream_t st = static_cast<hipStream_t>(stream);
+  hipError_t e = d == 256 ? launch_ext_d<256>(a, causal, st)
+               : d == 128 ? launch_ext_d<128>(a, causal, st)
+                          : launch_ext_d<64>(a, causal, st);
+  return e == hipSuccess ? FA_OK : FA_ERR_LAUNCH;
+}
+
 int run_bf16(const void* q, const void* k, const void* v, void* o, float* lse, int B, int H,
              int H_kv, int N, int d, float scale, int causal, int layout, void* stream) {
+  if (d == 256)  // the main kernel covers d = 64 and 128; d = 256 runs on the variant kernel
+    return run_ext(q, k, v, o, lse, B, H, H_kv, N, d, scale, causal, layout, -1, -1, nullptr,
+                   nullptr, 0, 0, 0, stream);
   const int rc = check_args(q, k, v, o, lse, B, H, H_kv, N, d, scale, causal, layout, 2);
   if (rc != FA_OK) return rc;
   fa::Bf16Args a;
@@ -224,6 +306,16 @@ hipError_t launch_bwd(fa::BwdArgs a, hipStream_t s) {
 }  // namespace
 
 extern "C" {
+
+int fa_fwd_ext(const void* q, const void* k, const void* v, void* o, float* lse, int B, int H,
+               int H_kv, int N, int d, float scale, int causal, int layout, int window_left,
+               int window_right, const float* alibi_slopes, const void* bias,
+               long long bias_batch_stride, long long bias_head_stride, long long bias_row_stride,
+               void* stream) {
+  return run_ext(q, k, v, o, lse, B, H, H_kv, N, d, scale, causal, layout, window_left,
+                 window_right, alibi_slopes, bias, bias_batch_stride, bias_head_stride,
+                 bias_row_stride, stream);
+}
 
 size_t fa_bwd_workspace_bytes(int B, int H, int H_kv, int N, int d) {
   if (B < 1 || H < 1 || N < 1 || N > kMaxN || (int64_t)B * H > kMaxBH) return 0;

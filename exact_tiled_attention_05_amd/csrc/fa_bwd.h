@@ -26,14 +26,11 @@
 //     are split over hsplit workgroups that write fp32 partial sums, and fa_bwd_combine_kernel
 //     adds them in split order (still deterministic).
 //
-// LDS layout of a 64-row tile: unpadded rows of 2d bytes; the 16-byte chunk j of row r is stored
-// at chunk position j ^ f(r). Tiles here are read both ways -- as rows (16 bytes of one row per
-// lane, 16 consecutive rows per group of lanes) and transposed (ds_read_b64_tr_b16: 8 bytes from
-// each of 8 rows x 64 bytes) -- and no padding serves both; the swizzle f below is chosen so that
-// both reads, and the staging writes, touch every bank equally often.
+// Tiles are read both as rows and transposed, so they use the swizzled LDS layout and the direct
+// global-to-LDS loads of fa_tiles.h.
 #pragma once
 
-#include "fa_device.h"
+#include "fa_tiles.h"
 
 namespace fa {
 
@@ -42,9 +39,6 @@ constexpr int kBwdQRows = 32 * kBwdQWaves;    // query rows per dQ workgroup
 constexpr int kBwdKvWaves = 8;                // dK/dV kernel: waves per workgroup
 constexpr int kBwdKvRows = 32 * kBwdKvWaves;  // keys per dK/dV workgroup
 constexpr int kBwdTile = 64;  // rows of a K/V tile (dQ kernel) or a Q/dO tile (dK/dV kernel)
-
-typedef unsigned int u32x4v __attribute__((ext_vector_type(4)));
-typedef float f32x4v __attribute__((ext_vector_type(4)));
 
 struct BwdArgs {
   const bf16* q;
@@ -67,97 +61,6 @@ struct BwdArgs {
   int q_rs, kv_rs;                     // element stride between consecutive rows of one head
 };
 
-// Swizzled tile geometry for head dim D (see the header comment).
-template <int D>
-struct Swz {
-  static constexpr int ROW = 2 * D;  // bytes per row
-  static constexpr int CPR = D / 8;  // 16-byte chunks per row
-  static constexpr int BYTES = kBwdTile * ROW;
-  // The LDS serves a 16-byte row read 16 lanes at a time (16 consecutive rows, one chunk each)
-  // and a transposing 8-byte read 32 lanes at a time (4 consecutive rows x 4 chunks of one
-  // 4-chunk group). d = 128 (16 chunks per 256-byte row): f must be injective on 16 consecutive
-  // rows, and 4 consecutive rows must move a chunk group to 4 different groups (f / 4 distinct):
-  // f(r) = 4 (r mod 4) + (r / 4) mod 4. d = 64 (8 chunks, two rows per 256 bytes): rows of equal
-  // parity share banks, so f must be injective on the 8 rows of one parity among 16, and rows r,
-  // r+2 must use different halves (bit 2 of f): f(r) = 4 ((r / 2) mod 2) + (r / 4) mod 4. Both
-  // also keep the staging writes (whole rows) conflict-free.
-  __device__ static __forceinline__ int f(int r) {
-    if constexpr (D == 128) return ((r & 3) << 2) | ((r >> 2) & 3);
-    else return (((r >> 1) & 1) << 2) | ((r >> 2) & 3);
-  }
-  __device__ static __forceinline__ int off(int r, int j) { return r * ROW + 16 * (j ^ f(r)); }
-};
-
-typedef int i32x4v __attribute__((ext_vector_type(4)));
-
-// Buffer resource (as four scalar registers, for the DMA instruction) over rows row0 .. N-1 of one
-// head, rows rs bytes apart, ending after row min(N, row0 + 64) - 1: bytes past it read as zeros.
-template <int D>
-__device__ __forceinline__ i32x4v tile_rsrc(const char* head, long long rs, int row0, int N) {
-  const int rows = min(N - row0, kBwdTile);  // >= 1: only tiles that start below N are loaded
-  const unsigned long long base = reinterpret_cast<unsigned long long>(head + (long long)row0 * rs);
-  i32x4v r;
-  r[0] = __builtin_amdgcn_readfirstlane((int)(base & 0xffffffffu));
-  r[1] = __builtin_amdgcn_readfirstlane((int)(base >> 32));
-  r[2] = __builtin_amdgcn_readfirstlane((int)((rows - 1) * rs) + 2 * D);
-  r[3] = 0x00020000;
-  return r;
-}
-
-// Global memory -> LDS without registers: one 16-byte buffer load per lane whose data the
-// hardware writes at (M0 + 16 * lane), i.e. 1 KB per wave instruction (rows 4p..4p+3 of the
-// swizzled tile for d = 128, 8p..8p+7 for d = 64, at LDS offset 1 KB * p). Lane l fills tile
-// position (row, slot) = (RPP p + l / CPR, l % CPR), so it fetches chunk slot ^ f(row) of that
-// row. The load counts on vmcnt; the caller waits for it before the barrier that publishes the
-// tile. (The DMA form is written as inline assembly: the compiler would otherwise wait for it
-// before every LDS access.)
-template <int D>
-__device__ __forceinline__ void dma_piece(char* tile, const i32x4v& rsrc, long long rs, int p,
-                                          int lane) {
-  constexpr int CPR = Swz<D>::CPR, RPP = 1024 / (2 * D);
-  const int rin = lane / CPR, slot = lane % CPR;
-  const unsigned voff = (unsigned)(rin * rs) + 16u * (unsigned)(slot ^ Swz<D>::f(RPP * p + rin));
-  const unsigned soff = __builtin_amdgcn_readfirstlane((int)(RPP * p * rs));
-  const unsigned m0 = __builtin_amdgcn_readfirstlane(
-      (int)((unsigned)(size_t)(FA_LDS char*)tile + 1024u * (unsigned)p));
-  asm volatile("s_mov_b32 m0, %0\n\tbuffer_load_dwordx4 %1, %2, %3 offen lds"
-               :: "s"(m0), "v"(voff), "s"(rsrc), "s"(soff) : "memory", "m0");
-}
-
-// The 64-row tile of rows row0.. by W waves (tile bytes / 1 KB pieces, spread over the waves).
-template <int D, int W>
-__device__ __forceinline__ void dma_tile(char* tile, const char* head, long long rs, int row0,
-                                         int N, int wave, int lane) {
-  constexpr int PIECES = Swz<D>::BYTES / 1024;
-  static_assert(PIECES % W == 0, "pieces must divide over the waves");
-  const i32x4v r = tile_rsrc<D>(head, rs, row0, N);
-#pragma unroll
-  for (int i = 0; i < PIECES / W; i++) dma_piece<D>(tile, r, rs, wave + W * i, lane);
-}
-
-__device__ __forceinline__ void wait_dma() { asm volatile("s_waitcnt vmcnt(0)" ::: "memory"); }
-
-// Row operand: 8 consecutive elements (chunk 2 dk + h) of tile row r.
-template <int D>
-__device__ __forceinline__ bf16x8 bwd_row(const char* tile, int r, int dk, int h) {
-  return lds_read_b128(tile + Swz<D>::off(r, 2 * dk + h));
-}
-
-// Transposed operand of one 16-row k-step: for lane (c, h) the 8 values of column 32 db + c from
-// rows r0 + {4h..4h+3, 8+4h..8+4h+3}, the row order of one k-step of the 32x32 accumulator.
-template <int D>
-__device__ __forceinline__ bf16x8 bwd_tr(const char* tile, int r0, int db, int lane) {
-  const int Lg = lane & 15, h = lane >> 5, hi = (lane >> 4) & 1;
-  const int col = 64 * db + 32 * hi + 8 * (Lg & 3);  // byte column
-  const int ra = r0 + 4 * h + (Lg >> 2), rb = ra + 8;
-  const bf16x4 x = lds_read_tr16(tile + Swz<D>::off(ra, col >> 4) + (col & 15));
-  const bf16x4 y = lds_read_tr16(tile + Swz<D>::off(rb, col >> 4) + (col & 15));
-  return __builtin_shufflevector(x, y, 0, 1, 2, 3, 4, 5, 6, 7);
-}
-
-// Row index (within a 32-row step) of accumulator register i of lane half h.
-__device__ __forceinline__ constexpr int acc_row(int i, int h) { return 8 * (i >> 2) + 4 * h + (i & 3); }
-
 // ---------------------------------------------------------------------------------------------
 // dQ (and D)
 // ---------------------------------------------------------------------------------------------
@@ -165,8 +68,8 @@ template <int D, bool CAUSAL>
 __global__ __launch_bounds__(kBwdQWaves * 64) __attribute__((amdgpu_waves_per_eu(2))) void fa_bwd_dq_kernel(BwdArgs a) {
   constexpr int DK = D / 16, DB = D / 32;
   using S = Swz<D>;
-  __shared__ __attribute__((aligned(1024))) char sK2[2][S::BYTES];  // two stages of K and V tiles
-  __shared__ __attribute__((aligned(1024))) char sV2[2][S::BYTES];
+  __shared__ __attribute__((aligned(1024))) char sK2[2][S::template bytes<kBwdTile>()];  // two stages of K and V tiles
+  __shared__ __attribute__((aligned(1024))) char sV2[2][S::template bytes<kBwdTile>()];
 
   const int tid = threadIdx.x, lane = tid & 63;
   const int wave = __builtin_amdgcn_readfirstlane(tid >> 6);  // uniform: keeps wave tests scalar
@@ -218,14 +121,14 @@ __global__ __launch_bounds__(kBwdQWaves * 64) __attribute__((amdgpu_waves_per_eu
   // tile j is computed (that stage's readers finished tile j-1 before the last barrier); one
   // barrier per tile.
   constexpr int W = kBwdQWaves;
-  dma_tile<D, W>(sK2[0], kh, rs, 0, N, wave, lane);
-  dma_tile<D, W>(sV2[0], vh, rs, 0, N, wave, lane);
+  dma_tile<D, kBwdTile, W>(sK2[0], kh, rs, 0, N, wave, lane);
+  dma_tile<D, kBwdTile, W>(sV2[0], vh, rs, 0, N, wave, lane);
   wait_dma();
   __syncthreads();
   for (int j = 0; j < n_kt; j++) {
     if (j + 1 < n_kt) {
-      dma_tile<D, W>(sK2[(j + 1) & 1], kh, rs, (j + 1) * kBwdTile, N, wave, lane);
-      dma_tile<D, W>(sV2[(j + 1) & 1], vh, rs, (j + 1) * kBwdTile, N, wave, lane);
+      dma_tile<D, kBwdTile, W>(sK2[(j + 1) & 1], kh, rs, (j + 1) * kBwdTile, N, wave, lane);
+      dma_tile<D, kBwdTile, W>(sV2[(j + 1) & 1], vh, rs, (j + 1) * kBwdTile, N, wave, lane);
     }
     const char* sK = sK2[j & 1];
     const char* sV = sV2[j & 1];
@@ -236,10 +139,10 @@ __global__ __launch_bounds__(kBwdQWaves * 64) __attribute__((amdgpu_waves_per_eu
       f32x16 st = f32x16{}, dpt = f32x16{};
 #pragma unroll
       for (int dk = 0; dk < DK; dk++)
-        st = __builtin_amdgcn_mfma_f32_32x32x16_bf16(bwd_row<D>(sK, 32 * sb + c, dk, h), qf[dk], st, 0, 0, 0);
+        st = __builtin_amdgcn_mfma_f32_32x32x16_bf16(tile_row<D>(sK, 32 * sb + c, dk, h), qf[dk], st, 0, 0, 0);
 #pragma unroll
       for (int dk = 0; dk < DK; dk++)
-        dpt = __builtin_amdgcn_mfma_f32_32x32x16_bf16(bwd_row<D>(sV, 32 * sb + c, dk, h), df[dk], dpt, 0, 0, 0);
+        dpt = __builtin_amdgcn_mfma_f32_32x32x16_bf16(tile_row<D>(sV, 32 * sb + c, dk, h), df[dk], dpt, 0, 0, 0);
       // P^T = exp(S^T scale - L), masked; dS^T = P^T (dP^T - D). Register i holds key
       // k0 + acc_row(i, h), visible iff acc_row(i, 0) <= lim (keys below N and, causal, <= qrow).
       const bool edge = (CAUSAL && k0 + 31 > qw0) || k0 + 31 >= N;  // wave-uniform
@@ -255,7 +158,7 @@ __global__ __launch_bounds__(kBwdQWaves * 64) __attribute__((amdgpu_waves_per_eu
       for (int ks = 0; ks < 2; ks++)
 #pragma unroll
         for (int db = 0; db < DB; db++)
-          acc[db] = __builtin_amdgcn_mfma_f32_32x32x16_bf16(bwd_tr<D>(sK, 32 * sb + 16 * ks, db, lane),
+          acc[db] = __builtin_amdgcn_mfma_f32_32x32x16_bf16(tile_tr<D>(sK, 32 * sb + 16 * ks, db, lane),
                                                             dsf[ks], acc[db], 0, 0, 0);
     }
     if (j + 1 < n_kt) {
@@ -285,8 +188,8 @@ template <int D, bool CAUSAL>
 __global__ __launch_bounds__(kBwdKvWaves * 64) __attribute__((amdgpu_waves_per_eu(2))) void fa_bwd_dkdv_kernel(BwdArgs a) {
   constexpr int DK = D / 16, DB = D / 32;
   using S = Swz<D>;
-  __shared__ __attribute__((aligned(1024))) char sQ2[2][S::BYTES];  // two stages of Q and dO tiles
-  __shared__ __attribute__((aligned(1024))) char sO2[2][S::BYTES];
+  __shared__ __attribute__((aligned(1024))) char sQ2[2][S::template bytes<kBwdTile>()];  // two stages of Q and dO tiles
+  __shared__ __attribute__((aligned(1024))) char sO2[2][S::template bytes<kBwdTile>()];
   __shared__ __attribute__((aligned(16))) float sL2[2][kBwdTile];    // L * log2(e)
   __shared__ __attribute__((aligned(16))) float sD2[2][kBwdTile];    // D
   __shared__ __attribute__((aligned(1024))) char sVb[kBwdKvRows * S::ROW];  // this block's V rows
@@ -336,9 +239,9 @@ __global__ __launch_bounds__(kBwdKvWaves * 64) __attribute__((amdgpu_waves_per_e
     const int g = g0 + s / (n_qt - t0), t = t0 + s % (n_qt - t0);
     const int bh = b * a.H + hk * a.group + g;
     const long long qhead = b * a.q_bs + (long long)(hk * a.group + g) * a.q_hs;
-    dma_tile<D, W>(sQ2[s & 1], reinterpret_cast<const char*>(a.q + qhead), rs, t * kBwdTile, N,
+    dma_tile<D, kBwdTile, W>(sQ2[s & 1], reinterpret_cast<const char*>(a.q + qhead), rs, t * kBwdTile, N,
                    wave, lane);
-    dma_tile<D, W>(sO2[s & 1], reinterpret_cast<const char*>(a.dout + qhead), rs, t * kBwdTile,
+    dma_tile<D, kBwdTile, W>(sO2[s & 1], reinterpret_cast<const char*>(a.dout + qhead), rs, t * kBwdTile,
                    N, wave, lane);
     if (tid < 2 * kBwdTile) {
       const int r = t * kBwdTile + (tid & (kBwdTile - 1));
@@ -375,7 +278,7 @@ __global__ __launch_bounds__(kBwdKvWaves * 64) __attribute__((amdgpu_waves_per_e
       f32x16 sc = f32x16{};
 #pragma unroll
       for (int dk = 0; dk < DK; dk++)
-        sc = __builtin_amdgcn_mfma_f32_32x32x16_bf16(bwd_row<D>(sQ, 32 * sb + c, dk, h), kf[dk], sc, 0, 0, 0);
+        sc = __builtin_amdgcn_mfma_f32_32x32x16_bf16(tile_row<D>(sQ, 32 * sb + c, dk, h), kf[dk], sc, 0, 0, 0);
       float p[16];
       bf16x8 pf[2];
 #pragma unroll
@@ -394,14 +297,14 @@ __global__ __launch_bounds__(kBwdKvWaves * 64) __attribute__((amdgpu_waves_per_e
       for (int ks = 0; ks < 2; ks++)
 #pragma unroll
         for (int db = 0; db < DB; db++)
-          accv[db] = __builtin_amdgcn_mfma_f32_32x32x16_bf16(bwd_tr<D>(sO, 32 * sb + 16 * ks, db, lane),
+          accv[db] = __builtin_amdgcn_mfma_f32_32x32x16_bf16(tile_tr<D>(sO, 32 * sb + 16 * ks, db, lane),
                                                              pf[ks], accv[db], 0, 0, 0);
       // dP = dO V^T, dS = P (dP - D), then dK^T += Q^T dS
       f32x16 dp = f32x16{};
 #pragma unroll
       for (int dk = 0; dk < DK; dk++)
-        dp = __builtin_amdgcn_mfma_f32_32x32x16_bf16(bwd_row<D>(sO, 32 * sb + c, dk, h),
-                                                     bwd_row<D>(sVb, 32 * wave + c, dk, h), dp, 0, 0, 0);
+        dp = __builtin_amdgcn_mfma_f32_32x32x16_bf16(tile_row<D>(sO, 32 * sb + c, dk, h),
+                                                     tile_row<D>(sVb, 32 * wave + c, dk, h), dp, 0, 0, 0);
       bf16x8 dsf[2];
 #pragma unroll
       for (int j4 = 0; j4 < 4; j4++) {
@@ -416,7 +319,7 @@ __global__ __launch_bounds__(kBwdKvWaves * 64) __attribute__((amdgpu_waves_per_e
       for (int ks = 0; ks < 2; ks++)
 #pragma unroll
         for (int db = 0; db < DB; db++)
-          acck[db] = __builtin_amdgcn_mfma_f32_32x32x16_bf16(bwd_tr<D>(sQ, 32 * sb + 16 * ks, db, lane),
+          acck[db] = __builtin_amdgcn_mfma_f32_32x32x16_bf16(tile_tr<D>(sQ, 32 * sb + 16 * ks, db, lane),
                                                              dsf[ks], acck[db], 0, 0, 0);
     }
     if (s + 1 < n_steps) {

@@ -1,0 +1,217 @@
+// Forward kernel for the score variants and for d = 256, gfx950.
+//
+// "Understanding FlashAttention Pt 1" writes the scores as S = QK^T / sqrt(d) + B, B an optional
+// additive mask or bias (§0.2), and lists local/sliding-window attention and ALiBi-style bias
+// among the variants a tiled kernel executes (§3.5, §4.2); "FlashAttention-2 -- Deeper Math" and
+// "Flash Attention" put the supported head dims at 64, 128 and 256. This kernel computes
+//     S_ij = scale q_i.k_j + B_ij - m_h |i - j|,   key j visible iff causal rule and
+//            i - window_left <= j <= i + window_right,
+// with the same tiled online softmax as the main kernel: S and P stay in registers, a running
+// maximum and sum per row, one division at the end, LSE = m + ln l. The bias B is a bf16 tensor
+// (any batch/head/row strides; stride 0 shares it), the ALiBi slopes m_h one fp32 per query head.
+// Tiles outside the window (or past the causal diagonal) are skipped for the whole workgroup, and
+// 32-key steps outside a wave's window for that wave (§3.5: only tiles crossing the boundary need
+// element-level masks).
+//
+// Structure: 4 waves x 32 query rows per workgroup (two workgroups per CU), queries outermost;
+// K/V tiles (64 keys, 32 for d = 256) go straight from memory into two swizzled LDS stages
+// (fa_tiles.h), one barrier per tile. Per 32-key step a wave forms S^T = K Q^T (keys on M, so a
+// lane holds 16 keys of one query row), adds the bias and ALiBi terms in fp32, masks, updates the
+// running maximum exactly (with the -inf reference guard of "Online Softmax & FlashAttention",
+// Listing 26.3), and accumulates O^T += V^T P^T with P rounded to bf16. A row that sees no key at
+// all (possible only through -inf bias entries) ends with O = 0 and LSE = -inf.
+#pragma once
+
+#include "fa_tiles.h"
+
+namespace fa {
+
+constexpr int kExtWaves = 4;
+constexpr int kExtRows = 32 * kExtWaves;  // query rows per workgroup
+constexpr int kExtNoWindow = 1 << 30;     // a window bound that never binds
+
+template <int D>
+struct ExtTile {
+  static constexpr int ROWS = D == 256 ? 32 : 64;  // keys per LDS tile
+};
+
+struct ExtArgs {
+  const bf16* q;
+  const bf16* k;
+  const bf16* v;
+  bf16* o;
+  float* lse;
+  const bf16* bias;      // optional additive bias (element strides below, columns contiguous)
+  const float* slopes;   // optional ALiBi slope per query head
+  long long bias_bs, bias_hs;
+  int bias_rs;
+  int N, H, Hkv, group, BH, n_qblk;
+  int wl, wr;            // window bounds (kExtNoWindow when unbounded)
+  float scale_log2;
+  long long q_bs, q_hs, kv_bs, kv_hs;
+  int q_rs, kv_rs;
+};
+
+template <int D, bool CAUSAL, bool ALIBI, bool BIAS>
+__global__ __launch_bounds__(kExtWaves * 64) __attribute__((amdgpu_waves_per_eu(D == 256 ? 1 : 2))) void fa_fwd_ext_kernel(ExtArgs a) {
+  constexpr int DK = D / 16, DB = D / 32;
+  constexpr int TK = ExtTile<D>::ROWS;
+  using S = Swz<D>;
+  __shared__ __attribute__((aligned(1024))) char sK2[2][S::template bytes<TK>()];
+  __shared__ __attribute__((aligned(1024))) char sV2[2][S::template bytes<TK>()];
+
+  const int tid = threadIdx.x, lane = tid & 63;
+  const int wave = __builtin_amdgcn_readfirstlane(tid >> 6);
+  const int c = lane & 31, h = lane >> 5;
+  int bh, qblk;
+  map_block<CAUSAL>(blockIdx.x, gridDim.x, a.BH, a.n_qblk, bh, qblk);
+  const int b = bh / a.H, hq = bh - b * a.H, hk = hq / a.group;
+  const int N = a.N;
+  const int bq0 = qblk * kExtRows, bq1 = min(N - 1, bq0 + kExtRows - 1);  // workgroup rows
+  const int wq0 = bq0 + 32 * wave, wq1 = wq0 + 31;                        // wave rows
+  const int qrow = wq0 + c;
+  const long long qoff = b * a.q_bs + hq * a.q_hs + (long long)qrow * a.q_rs;
+  const long long kvhead = b * a.kv_bs + hk * a.kv_hs;
+  const long long rs = 2LL * a.kv_rs;
+
+  // Keys the workgroup / the wave can see: [lo, hi] from the window and the causal rule.
+  auto key_lo = [&](int q0) { return max(0, q0 - a.wl); };
+  auto key_hi = [&](int q1) {
+    int x = min(N - 1, q1 + a.wr);
+    return CAUSAL ? min(x, q1) : x;
+  };
+  const int blo = key_lo(bq0), bhi = key_hi(bq1);
+  const int wlo = key_lo(wq0), whi = key_hi(min(wq1, N - 1));
+
+  bf16x8 qf[DK];
+#pragma unroll
+  for (int dk = 0; dk < DK; dk++)
+    qf[dk] = qrow < N ? *reinterpret_cast<const bf16x8*>(a.q + qoff + dk * 16 + h * 8) : bf16x8{};
+  float slope2 = 0.f;
+  if constexpr (ALIBI) slope2 = a.slopes[hq] * kLog2e;
+  // bias row of this lane's query (buffer resource over this head's matrix: rows past N and the
+  // columns past the last row's end read as zeros; columns past N are masked anyway)
+  __amdgpu_buffer_rsrc_t brs;
+  if constexpr (BIAS) {
+    const bf16* bh0 = a.bias + b * a.bias_bs + hq * a.bias_hs;
+    brs = __builtin_amdgcn_make_buffer_rsrc((void*)bh0, 0,
+                                            (int)(((long long)(N - 1) * a.bias_rs + N) * 2),
+                                            0x00020000);
+  }
+  auto load_bias = [&](int k0, bf16x4 (&bv)[4]) {
+#pragma unroll
+    for (int j4 = 0; j4 < 4; j4++)
+      bv[j4] = __builtin_bit_cast(bf16x4, __builtin_amdgcn_raw_buffer_load_b64(
+                   brs, (int)(((long long)qrow * a.bias_rs + k0 + 8 * j4 + 4 * h) * 2), 0, 0));
+  };
+
+  f32x16 acc[DB];
+#pragma unroll
+  for (int db = 0; db < DB; db++) acc[db] = f32x16{};
+  float m2 = -INFINITY, l = 0.f;
+
+  const char* kh = reinterpret_cast<const char*>(a.k + kvhead);
+  const char* vh = reinterpret_cast<const char*>(a.v + kvhead);
+  const int t_first = blo / TK, t_last = bhi / TK;  // tiles with a key some row of the block sees
+  if (t_first <= t_last) {
+    dma_tile<D, TK, kExtWaves>(sK2[0], kh, rs, t_first * TK, N, wave, lane);
+    dma_tile<D, TK, kExtWaves>(sV2[0], vh, rs, t_first * TK, N, wave, lane);
+    wait_dma();
+    __syncthreads();
+  }
+  for (int t = t_first; t <= t_last; t++) {
+    const int st = (t - t_first) & 1;
+    if (t < t_last) {
+      dma_tile<D, TK, kExtWaves>(sK2[st ^ 1], kh, rs, (t + 1) * TK, N, wave, lane);
+      dma_tile<D, TK, kExtWaves>(sV2[st ^ 1], vh, rs, (t + 1) * TK, N, wave, lane);
+    }
+    const char* sK = sK2[st];
+    const char* sV = sV2[st];
+#pragma unroll
+    for (int sb = 0; sb < TK / 32; sb++) {
+      const int k0 = t * TK + 32 * sb;
+      // wave-uniform: no key of this step is visible to any row of the wave
+      if (wq0 >= N || k0 > whi || k0 + 31 < wlo) continue;
+      bf16x4 bcur[4];
+      if constexpr (BIAS) load_bias(k0, bcur);  // in flight during the QK products
+      f32x16 sc = f32x16{};
+#pragma unroll
+      for (int dk = 0; dk < DK; dk++)
+        sc = __builtin_amdgcn_mfma_f32_32x32x16_bf16(tile_row<D>(sK, 32 * sb + c, dk, h), qf[dk], sc, 0, 0, 0);
+      // scores in log2 units: x = scale log2(e) s + log2(e) (B - m |i - j|); register i is key
+      // k0 + acc_row(i, h) of query qrow
+      float x[16];
+      const float dq = (float)(qrow - k0 - 4 * h);  // qrow - key = dq - acc_row(i, 0)
+#pragma unroll
+      for (int i = 0; i < 16; i++) {
+        float xi = sc[i] * a.scale_log2;
+        if constexpr (BIAS) {
+          const float bi = (float)bcur[i >> 2][i & 3];
+          xi = __builtin_fmaf(bi, kLog2e, xi);
+        }
+        if constexpr (ALIBI) xi = __builtin_fmaf(-slope2, __builtin_fabsf(dq - (float)acc_row(i, 0)), xi);
+        x[i] = xi;
+      }
+      // mask: keys past N, past the causal diagonal or outside the window (only steps that cross
+      // one of those bounds for some row of the wave)
+      const bool edge = k0 + 31 > min(N - 1, CAUSAL ? wq0 : N - 1) || k0 + 31 > wq0 + a.wr ||
+                        k0 < wq1 - a.wl;
+      if (edge) {
+        const int lo = qrow - a.wl - k0 - 4 * h;  // visible iff lo <= acc_row(i, 0) <= hi
+        const int hi = min(N - 1, min(CAUSAL ? qrow : N - 1, qrow + a.wr)) - k0 - 4 * h;
+#pragma unroll
+        for (int i = 0; i < 16; i++)
+          x[i] = (acc_row(i, 0) >= lo && acc_row(i, 0) <= hi) ? x[i] : -INFINITY;
+      }
+      float mx = x[0];
+#pragma unroll
+      for (int i = 1; i < 16; i++) mx = __builtin_fmaxf(mx, x[i]);
+      mx = half_swap_max(mx);
+      const float mn = __builtin_fmaxf(m2, mx);
+      const float ref = mn == -INFINITY ? 0.f : mn;
+      if (__any(mn > m2)) {
+        const float alpha = m2 == -INFINITY ? 0.f : fast_exp2(m2 - ref);
+        l *= alpha;
+#pragma unroll
+        for (int db = 0; db < DB; db++) acc[db] *= alpha;
+      }
+      m2 = mn;
+      float p[16];
+      bf16x8 pf[2];
+#pragma unroll
+      for (int i = 0; i < 16; i++) {
+        p[i] = fast_exp2(x[i] - ref);
+        pf[i >> 3][i & 7] = (bf16)p[i];
+      }
+      l += sum16(p);
+#pragma unroll
+      for (int ks = 0; ks < 2; ks++)
+#pragma unroll
+        for (int db = 0; db < DB; db++)
+          acc[db] = __builtin_amdgcn_mfma_f32_32x32x16_bf16(tile_tr<D>(sV, 32 * sb + 16 * ks, db, lane),
+                                                            pf[ks], acc[db], 0, 0, 0);
+    }
+    if (t < t_last) {
+      wait_dma();
+      __syncthreads();
+    }
+  }
+
+  const float lt = half_swap_sum(l);
+  if (qrow < N) {
+    const float inv = lt > 0.f ? 1.0f / lt : 0.f;
+    bf16* orow = a.o + qoff;
+#pragma unroll
+    for (int db = 0; db < DB; db++)
+#pragma unroll
+      for (int g4 = 0; g4 < 4; g4++) {
+        bf16x4 ov;
+#pragma unroll
+        for (int e = 0; e < 4; e++) ov[e] = (bf16)(acc[db][4 * g4 + e] * inv);
+        *reinterpret_cast<bf16x4*>(orow + 32 * db + 8 * g4 + 4 * h) = ov;
+      }
+    if (h == 0) a.lse[(long long)bh * N + qrow] = lt > 0.f ? kLn2 * (m2 + fast_log2(lt)) : -INFINITY;
+  }
+}
+
+}  // namespace fa

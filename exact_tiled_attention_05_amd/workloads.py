@@ -21,7 +21,12 @@ layer decoding: one new query token per sequence (Nq = 1) against N = 32768 cach
 batch of 8 sequences ("FlashAttention-2 -- Deeper Math", "What FA-2 does not fix"); Q is then drawn
 with Nq rows. The two "_bwd" workloads are the Llama layer (with and without grouped K/V heads)
 run backward ("Understanding FlashAttention Pt 1", §3.6): the same Q, K, V recipe and seeds as the
-forward workloads, plus an upstream gradient dO drawn like Q from its own seed.
+forward workloads, plus an upstream gradient dO drawn like Q from its own seed. Four more exercise
+the score variants and the largest head dim ("Understanding FlashAttention Pt 1", §0.2, §3.5, §4.2;
+"Flash Attention": head dims up to 256): a d = 256 layer (16 heads, N = 8192, causal); the
+grouped Llama layer with a causal sliding window of 4096 keys (each query sees itself and the 4095
+keys before it); the Llama layer with ALiBi slopes 2^(-8 (h + 1) / H); and a non-causal layer with
+an additive bf16 bias of its own seed, N(0, 1), one [N, N] matrix per head.
 """
 import math
 
@@ -40,6 +45,14 @@ WORKLOADS = {
                                      causal=(True,), seed=5, layout="bnhd", sample_rows=64),
     "llama3_8b_gqa_decode_b8_n32k": dict(B=8, H=32, H_kv=8, Nq=1, N=32768, d=128, dtype="bf16",
                                          causal=(True,), seed=6, layout="bnhd"),
+    "d256_h16_n8k_causal": dict(B=1, H=16, N=8192, d=256, dtype="bf16", causal=(True,), seed=7,
+                                sample_rows=64),
+    "llama3_8b_gqa_n8k_swa4k": dict(B=1, H=32, H_kv=8, N=8192, d=128, dtype="bf16", causal=(True,),
+                                    seed=5, layout="bnhd", window=(4095, -1), sample_rows=64),
+    "llama3_8b_n8k_causal_alibi": dict(B=1, H=32, N=8192, d=128, dtype="bf16", causal=(True,),
+                                       seed=2, alibi=True, sample_rows=64),
+    "b1h16_n4k_bias": dict(B=1, H=16, N=4096, d=128, dtype="bf16", causal=(False,), seed=8,
+                           bias_seed=18, sample_rows=64),
     "llama3_8b_n8k_causal_bwd": dict(B=1, H=32, N=8192, d=128, dtype="bf16", causal=(True,),
                                      seed=2, grad_seed=12, backward=True),
     "llama3_8b_gqa_n8k_causal_bwd": dict(B=1, H=32, H_kv=8, N=8192, d=128, dtype="bf16",
@@ -122,6 +135,40 @@ def workload_inputs(name):
     w = WORKLOADS[name]
     q, k, v = make_inputs(**w)
     return q, k, v, softmax_scale(w["d"])
+
+
+def alibi_slopes(H):
+    """The geometric ALiBi slopes 2^(-8 (h + 1) / H), h = 0 .. H-1, as float32 values."""
+    return torch.tensor([2.0 ** (-8.0 * (h + 1) / H) for h in range(H)], dtype=torch.float32)
+
+
+def workload_bias(name):
+    """The additive bias [1, H, N, N] (bf16, N(0, 1)) of a bias workload."""
+    w = WORKLOADS[name]
+    g = torch.Generator().manual_seed(w["bias_seed"])
+    return torch.randn((1, w["H"], w["N"], w["N"]), generator=g).to(torch.bfloat16)
+
+
+def visible_pairs(N, causal, window=None):
+    """Number of (query, key) pairs a row-wise mask leaves visible in one [N, N] head: query i sees
+    keys max(0, i - left) .. min(N - 1, i + right), capped at i when causal."""
+    i = torch.arange(N, dtype=torch.int64)
+    lo = torch.zeros_like(i)
+    hi = torch.full_like(i, N - 1)
+    if window is not None:
+        if window[0] >= 0:
+            lo = torch.clamp(i - window[0], min=0)
+        if window[1] >= 0:
+            hi = torch.clamp(i + window[1], max=N - 1)
+    if causal:
+        hi = torch.minimum(hi, i)
+    return int((hi - lo + 1).clamp(min=0).sum())
+
+
+def metric_flops_masked(B, H, N, d, causal, window=None):
+    """4*d FLOPs per visible (query, key) pair: the two products restricted to what the mask
+    keeps. Equals metric_flops up to the diagonal's N/2 pairs when there is no window."""
+    return 4.0 * B * H * d * visible_pairs(N, causal, window)
 
 
 def workload_grad(name):

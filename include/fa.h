@@ -99,6 +99,30 @@ int fa_fwd_gqa_f32(const float* q, const float* k, const float* v, float* o, flo
                    void* stream);
 
 /*
+ * Score variants ("Understanding FlashAttention Pt 1": S = QK^T / sqrt(d) + B with B an optional
+ * additive mask or bias, §0.2; local/sliding-window attention and ALiBi-style bias, §3.5 and §4.2)
+ * and head dim 256 ("Flash Attention": supported head dims 64, 128, 256). fa_fwd_ext is fa_fwd_gqa
+ * (same layouts, head grouping, outputs and codes) with, for query row i and key j of one head:
+ *   window_left, window_right: key j is visible iff i - window_left <= j <= i + window_right;
+ *       -1 leaves that side unbounded (both -1: no window); the causal rule still applies when
+ *       causal = 1. Tiles outside the window are skipped.
+ *   alibi_slopes: NULL or device fp32[H], slope m_h of query head h: the score gets - m_h |i - j|.
+ *   bias: NULL or device bf16 matrix per (batch, query head): the score gets bias[b][h][i][j] at
+ *       element offset b * bias_batch_stride + h * bias_head_stride + i * bias_row_stride + j;
+ *       a stride of 0 shares the matrix across batches or heads; bias_row_stride >= N and a
+ *       multiple of 4, the pointer 8-byte aligned (else FA_ERR_INVALID_ARG / FA_ERR_ALIGNMENT);
+ *       one head's matrix must span under 2 GiB (else FA_ERR_UNSUPPORTED). -inf entries mask.
+ * The bias and ALiBi terms are added to the scaled score: S_ij = scale q_i.k_j + B_ij - m_h|i-j|.
+ * A row with no visible key (only possible through -inf bias entries) gets O = 0 and
+ * LSE = -inf. d in {64, 128, 256}; bf16 only. fa_fwd and fa_fwd_gqa also accept d = 256 (bf16).
+ */
+int fa_fwd_ext(const void* q, const void* k, const void* v, void* o, float* lse, int B, int H,
+               int H_kv, int N, int d, float scale, int causal, int layout, int window_left,
+               int window_right, const float* alibi_slopes, const void* bias,
+               long long bias_batch_stride, long long bias_head_stride, long long bias_row_stride,
+               void* stream);
+
+/*
  * Split-KV decoding ("FlashAttention-2 -- Deeper Math", "What FA-2 does not fix": few queries
  * against a long K/V sequence are bound by reading K and V, so the keys are split across the GPU
  * and the partial softmaxes merged with the blockwise recurrence of "Understanding FlashAttention

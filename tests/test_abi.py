@@ -26,8 +26,8 @@ def _codes():
 
 
 def test_header_declares_the_expected_entry_points():
-    assert _declared() == ["fa_bwd", "fa_bwd_workspace_bytes", "fa_fwd", "fa_fwd_f32",
-                           "fa_fwd_gqa", "fa_fwd_gqa_f32", "fa_fwd_splitkv",
+    assert _declared() == ["fa_bwd", "fa_bwd_workspace_bytes", "fa_fwd", "fa_fwd_ext",
+                           "fa_fwd_f32", "fa_fwd_gqa", "fa_fwd_gqa_f32", "fa_fwd_splitkv",
                            "fa_splitkv_workspace_bytes", "fa_strerror", "fa_version"]
 
 
@@ -79,7 +79,7 @@ BAD = [
     (dict(scale=float("inf")), fa.FA_ERR_INVALID_ARG),
     (dict(scale=float("nan")), fa.FA_ERR_INVALID_ARG),
     (dict(d=96), fa.FA_ERR_UNSUPPORTED),
-    (dict(d=256), fa.FA_ERR_UNSUPPORTED),
+    (dict(d=512), fa.FA_ERR_UNSUPPORTED),
     (dict(d=0), fa.FA_ERR_UNSUPPORTED),
     (dict(q=Q + 8), fa.FA_ERR_ALIGNMENT),
     (dict(lse=L + 4), fa.FA_ERR_ALIGNMENT),
@@ -274,3 +274,46 @@ def test_backward_binding_checks_tensors_before_calling():
         fa.backward(q, q, q, q[:, :, :4].contiguous(), lse, q)  # o's shape differs from q's
     with pytest.raises(ValueError):
         fa.backward(q, q, q, q, lse, q)  # CPU tensors (shapes are fine)
+
+
+# ---- score variants -------------------------------------------------------------------------------
+SL_, BI_ = A + 15 * (1 << 32), A + 16 * (1 << 32)
+GOOD_EXT = dict(q=Q, k=K, v=V, o=O, lse=L, B=2, H=8, H_kv=2, N=300, d=128, scale=0.1, causal=1,
+                layout=0, wl=64, wr=-1, slopes=SL_, bias=BI_, bbs=0, bhs=300 * 304, brs=304)
+
+
+def _call_ext(**kw):
+    a = dict(GOOD_EXT, **kw)
+    return fa.fa_fwd_ext(a["q"], a["k"], a["v"], a["o"], a["lse"], a["B"], a["H"], a["H_kv"],
+                         a["N"], a["d"], a["scale"], a["causal"], a["layout"], a["wl"], a["wr"],
+                         a["slopes"], a["bias"], a["bbs"], a["bhs"], a["brs"], None)
+
+
+BAD_EXT = [
+    (dict(wl=-2), fa.FA_ERR_INVALID_ARG),
+    (dict(wr=-5), fa.FA_ERR_INVALID_ARG),
+    (dict(d=96), fa.FA_ERR_UNSUPPORTED),
+    (dict(brs=299), fa.FA_ERR_INVALID_ARG),          # rows shorter than N
+    (dict(brs=302), fa.FA_ERR_ALIGNMENT),             # row stride not a multiple of 4
+    (dict(bias=BI_ + 2), fa.FA_ERR_ALIGNMENT),
+    (dict(bhs=-1), fa.FA_ERR_INVALID_ARG),
+    (dict(slopes=SL_ + 2), fa.FA_ERR_ALIGNMENT),
+    (dict(N=40000, brs=40000, bhs=0), fa.FA_ERR_UNSUPPORTED),  # one matrix over 2 GiB
+    (dict(bias=O), fa.FA_ERR_INVALID_ARG),            # bias overlaps o
+    (dict(slopes=L), fa.FA_ERR_INVALID_ARG),          # slopes overlap lse
+    (dict(H_kv=3), fa.FA_ERR_INVALID_ARG),
+]
+
+
+@pytest.mark.parametrize("kw,code", BAD_EXT, ids=[str(b[0]) for b in BAD_EXT])
+def test_bad_variant_arguments_are_refused(kw, code):
+    assert _call_ext(**kw) == code
+
+
+def test_d256_is_accepted_by_the_bf16_forward_only():
+    # the fp32 path refuses d = 256 before any HIP call
+    assert fa.fa_fwd_f32(Q, K, V, O, L, 1, 2, 64, 256, 0.1, 0, None) == fa.FA_ERR_UNSUPPORTED
+    assert fa.fa_fwd_gqa_f32(Q, K, V, O, L, 1, 2, 2, 64, 256, 0.1, 0, 0, None) == \
+        fa.FA_ERR_UNSUPPORTED
+    assert fa.fa_bwd(Q, K, V, O, DO_, L, DQ_, DK_, DV_, 1, 2, 2, 64, 256, 0.1, 0, 0, WB_, 1 << 30,
+                     None) == fa.FA_ERR_UNSUPPORTED
