@@ -154,7 +154,9 @@ int run_ext(const void* q, const void* k, const void* v, void* o, float* lse, in
   a.n_qblk = (N + fa::kExtRows - 1) / fa::kExtRows;
   a.wl = window_left < 0 ? fa::kExtNoWindow : std::min(window_left, N);
   a.wr = window_right < 0 ? fa::kExtNoWindow : std::min(window_right, N);
-  a.scale_log2 = scale * fa::kLog2e;
+  // scale 0 runs as the smallest normal float (as in run_bf16): the raw-score maximum of a masked
+  // step stays -inf instead of 0 * inf
+  a.scale_log2 = scale > 0.f ? scale * fa::kLog2e : FLT_MIN;
   const Strides sq = strides_of(layout, H, N, d), sk = strides_of(layout, H_kv, N, d);
   a.q_bs = sq.bs;
   a.q_hs = sq.hs;

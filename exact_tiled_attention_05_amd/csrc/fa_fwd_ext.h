@@ -16,11 +16,13 @@
 // Structure: 4 waves x 32 query rows per workgroup (two workgroups per CU), queries outermost;
 // K/V tiles (64 keys, 32 for d = 256) go straight from memory into two swizzled LDS stages
 // (fa_tiles.h), one barrier per tile. Per 32-key step a wave forms S^T = K Q^T (keys on M, so a
-// lane holds 16 keys of one query row), adds the bias and ALiBi terms in fp32, masks, updates the
-// running maximum exactly (with the -inf reference guard of "Online Softmax & FlashAttention",
-// Listing 26.3), and accumulates O^T += V^T P^T with P rounded to bf16. A row that sees no key at
+// lane holds 16 keys of one query row), adds the bias and ALiBi terms in fp32, masks, moves the
+// running reference lazily (as the main kernel does; with the -inf reference guard of "Online
+// Softmax & FlashAttention", Listing 26.3), and accumulates O^T += V^T P^T with P rounded to bf16. A row that sees no key at
 // all (possible only through -inf bias entries) ends with O = 0 and LSE = -inf.
 #pragma once
+
+#include <type_traits>
 
 #include "fa_tiles.h"
 
@@ -29,6 +31,17 @@ namespace fa {
 constexpr int kExtWaves = 4;
 constexpr int kExtRows = 32 * kExtWaves;  // query rows per workgroup
 constexpr int kExtNoWindow = 1 << 30;     // a window bound that never binds
+constexpr float kExtSlack = 2.f;          // lazy reference: moved when exceeded by > 2 (log2)
+
+__device__ __forceinline__ float max16_arr(const float (&v)[16]) {
+  float a = __builtin_fmaxf(__builtin_fmaxf(v[0], v[1]), v[2]);
+  float b = __builtin_fmaxf(__builtin_fmaxf(v[3], v[4]), v[5]);
+  float c = __builtin_fmaxf(__builtin_fmaxf(v[6], v[7]), v[8]);
+  float d = __builtin_fmaxf(__builtin_fmaxf(v[9], v[10]), v[11]);
+  float e = __builtin_fmaxf(__builtin_fmaxf(v[12], v[13]), v[14]);
+  return __builtin_fmaxf(__builtin_fmaxf(__builtin_fmaxf(a, b), c),
+                         __builtin_fmaxf(__builtin_fmaxf(d, e), v[15]));
+}
 
 template <int D>
 struct ExtTile {
@@ -87,6 +100,8 @@ __global__ __launch_bounds__(kExtWaves * 64) __attribute__((amdgpu_waves_per_eu(
 #pragma unroll
   for (int dk = 0; dk < DK; dk++)
     qf[dk] = qrow < N ? *reinterpret_cast<const bf16x8*>(a.q + qoff + dk * 16 + h * 8) : bf16x8{};
+  LaneOffsets<D> lo_;
+  lo_.init(lane);
   float slope2 = 0.f;
   if constexpr (ALIBI) slope2 = a.slopes[hq] * kLog2e;
   // bias row of this lane's query (buffer resource over this head's matrix: rows past N and the
@@ -119,8 +134,10 @@ __global__ __launch_bounds__(kExtWaves * 64) __attribute__((amdgpu_waves_per_eu(
     wait_dma();
     __syncthreads();
   }
-  for (int t = t_first; t <= t_last; t++) {
-    const int st = (t - t_first) & 1;
+  // Tile t sits in stage (t - t_first) % 2; the stage is a compile-time constant of each copy of
+  // the loop body, so every LDS address is a per-lane offset plus an immediate.
+  auto tile = [&](auto stage_c, int t) {
+    constexpr int st = decltype(stage_c)::value;
     if (t < t_last) {
       dma_tile<D, TK, kExtWaves>(sK2[st ^ 1], kh, rs, (t + 1) * TK, N, wave, lane);
       dma_tile<D, TK, kExtWaves>(sV2[st ^ 1], vh, rs, (t + 1) * TK, N, wave, lane);
@@ -131,56 +148,67 @@ __global__ __launch_bounds__(kExtWaves * 64) __attribute__((amdgpu_waves_per_eu(
     for (int sb = 0; sb < TK / 32; sb++) {
       const int k0 = t * TK + 32 * sb;
       // wave-uniform: no key of this step is visible to any row of the wave
-      if (wq0 >= N || k0 > whi || k0 + 31 < wlo) continue;
+      if (wq0 >= N || k0 > whi || k0 + 31 < wlo) continue;  // (continue: next sb)
       bf16x4 bcur[4];
       if constexpr (BIAS) load_bias(k0, bcur);  // in flight during the QK products
       f32x16 sc = f32x16{};
 #pragma unroll
       for (int dk = 0; dk < DK; dk++)
-        sc = __builtin_amdgcn_mfma_f32_32x32x16_bf16(tile_row<D>(sK, 32 * sb + c, dk, h), qf[dk], sc, 0, 0, 0);
-      // scores in log2 units: x = scale log2(e) s + log2(e) (B - m |i - j|); register i is key
-      // k0 + acc_row(i, h) of query qrow
-      float x[16];
-      const float dq = (float)(qrow - k0 - 4 * h);  // qrow - key = dq - acc_row(i, 0)
-#pragma unroll
-      for (int i = 0; i < 16; i++) {
-        float xi = sc[i] * a.scale_log2;
-        if constexpr (BIAS) {
-          const float bi = (float)bcur[i >> 2][i & 3];
-          xi = __builtin_fmaf(bi, kLog2e, xi);
-        }
-        if constexpr (ALIBI) xi = __builtin_fmaf(-slope2, __builtin_fabsf(dq - (float)acc_row(i, 0)), xi);
-        x[i] = xi;
-      }
-      // mask: keys past N, past the causal diagonal or outside the window (only steps that cross
-      // one of those bounds for some row of the wave)
+        sc = __builtin_amdgcn_mfma_f32_32x32x16_bf16(tile_row_at<D>(sK, lo_, 32 * sb, dk), qf[dk], sc, 0, 0, 0);
+      // mask bounds: keys past N, past the causal diagonal or outside the window (only steps that
+      // cross one of those bounds for some row of the wave); register i is key k0 + acc_row(i, h)
       const bool edge = k0 + 31 > min(N - 1, CAUSAL ? wq0 : N - 1) || k0 + 31 > wq0 + a.wr ||
                         k0 < wq1 - a.wl;
-      if (edge) {
-        const int lo = qrow - a.wl - k0 - 4 * h;  // visible iff lo <= acc_row(i, 0) <= hi
-        const int hi = min(N - 1, min(CAUSAL ? qrow : N - 1, qrow + a.wr)) - k0 - 4 * h;
+      const int lo = qrow - a.wl - k0 - 4 * h;  // visible iff lo <= acc_row(i, 0) <= hi
+      const int hi = min(N - 1, min(CAUSAL ? qrow : N - 1, qrow + a.wr)) - k0 - 4 * h;
+      float t2;                   // this step's row maximum in log2 units (-inf: nothing visible)
+      float x[16];                // scores in log2 units, or raw scores (PLAIN)
+      constexpr bool PLAIN = !ALIBI && !BIAS;
+      if constexpr (PLAIN) {
+        // raw scores: the maximum commutes with the positive scale, which is fused into the
+        // exponent below
 #pragma unroll
-        for (int i = 0; i < 16; i++)
-          x[i] = (acc_row(i, 0) >= lo && acc_row(i, 0) <= hi) ? x[i] : -INFINITY;
+        for (int i = 0; i < 16; i++) x[i] = sc[i];
+        if (edge) {  // wave-uniform: most steps cross no bound and skip the masks
+#pragma unroll
+          for (int i = 0; i < 16; i++)
+            x[i] = (acc_row(i, 0) >= lo && acc_row(i, 0) <= hi) ? x[i] : -INFINITY;
+        }
+        t2 = half_swap_max(max16_arr(x)) * a.scale_log2;
+      } else {
+        // x = scale log2(e) s + log2(e) (B - m |i - j|)
+        const float dq = (float)(qrow - k0 - 4 * h);  // qrow - key = dq - acc_row(i, 0)
+#pragma unroll
+        for (int i = 0; i < 16; i++) {
+          float xi = sc[i] * a.scale_log2;
+          if constexpr (BIAS) xi = __builtin_fmaf((float)bcur[i >> 2][i & 3], kLog2e, xi);
+          if constexpr (ALIBI) xi = __builtin_fmaf(-slope2, __builtin_fabsf(dq - (float)acc_row(i, 0)), xi);
+          x[i] = xi;
+        }
+        if (edge) {
+#pragma unroll
+          for (int i = 0; i < 16; i++)
+            x[i] = (acc_row(i, 0) >= lo && acc_row(i, 0) <= hi) ? x[i] : -INFINITY;
+        }
+        t2 = half_swap_max(max16_arr(x));
       }
-      float mx = x[0];
-#pragma unroll
-      for (int i = 1; i < 16; i++) mx = __builtin_fmaxf(mx, x[i]);
-      mx = half_swap_max(mx);
-      const float mn = __builtin_fmaxf(m2, mx);
-      const float ref = mn == -INFINITY ? 0.f : mn;
-      if (__any(mn > m2)) {
-        const float alpha = m2 == -INFINITY ? 0.f : fast_exp2(m2 - ref);
+      // Running reference, moved only when a score exceeds it by more than kExtSlack (log2 units):
+      // any reference gives the same softmax, and the accumulator rescale is skipped wave-wide
+      // otherwise (p <= 2^kExtSlack). The -inf guard keeps rows that have seen nothing at 0.
+      if (__any(t2 > m2 + kExtSlack)) {
+        const float mn = __builtin_fmaxf(m2, t2);
+        const float alpha = m2 == -INFINITY ? 0.f : fast_exp2(m2 - mn);
         l *= alpha;
 #pragma unroll
         for (int db = 0; db < DB; db++) acc[db] *= alpha;
+        m2 = mn;
       }
-      m2 = mn;
+      const float ref = m2 == -INFINITY ? 0.f : m2;
       float p[16];
       bf16x8 pf[2];
 #pragma unroll
       for (int i = 0; i < 16; i++) {
-        p[i] = fast_exp2(x[i] - ref);
+        p[i] = PLAIN ? fast_exp2(__builtin_fmaf(x[i], a.scale_log2, -ref)) : fast_exp2(x[i] - ref);
         pf[i >> 3][i & 7] = (bf16)p[i];
       }
       l += sum16(p);
@@ -188,13 +216,17 @@ __global__ __launch_bounds__(kExtWaves * 64) __attribute__((amdgpu_waves_per_eu(
       for (int ks = 0; ks < 2; ks++)
 #pragma unroll
         for (int db = 0; db < DB; db++)
-          acc[db] = __builtin_amdgcn_mfma_f32_32x32x16_bf16(tile_tr<D>(sV, 32 * sb + 16 * ks, db, lane),
+          acc[db] = __builtin_amdgcn_mfma_f32_32x32x16_bf16(tile_tr_at<D>(sV, lo_, 32 * sb + 16 * ks, db),
                                                             pf[ks], acc[db], 0, 0, 0);
     }
     if (t < t_last) {
       wait_dma();
       __syncthreads();
     }
+  };
+  for (int t = t_first; t <= t_last; t += 2) {
+    tile(std::integral_constant<int, 0>{}, t);
+    if (t + 1 <= t_last) tile(std::integral_constant<int, 1>{}, t + 1);
   }
 
   const float lt = half_swap_sum(l);

@@ -107,6 +107,41 @@ __device__ __forceinline__ bf16x8 tile_tr(const char* tile, int r0, int db, int 
   return __builtin_shufflevector(x, y, 0, 1, 2, 3, 4, 5, 6, 7);
 }
 
+// Per-lane byte offsets of those reads, computed once. The swizzle depends on the row only
+// through r mod 16, so a read at row offset 16 k (k a compile-time step index) is the lane's
+// offset plus the immediate 16 k * ROW: no address arithmetic in the loops.
+template <int D>
+struct LaneOffsets {
+  int row[D / 16];     // row c, chunk 2 dk + h
+  int tr[D / 32][2];   // transposing reads of rows 4h + L/4 (and + 8) of a 16-row k-step, block db
+  __device__ __forceinline__ void init(int lane) {
+    const int c = lane & 31, h = lane >> 5, Lg = lane & 15, hi = (lane >> 4) & 1;
+#pragma unroll
+    for (int dk = 0; dk < D / 16; dk++) row[dk] = Swz<D>::off(c, 2 * dk + h);
+#pragma unroll
+    for (int db = 0; db < D / 32; db++) {
+      const int col = 64 * db + 32 * hi + 8 * (Lg & 3);
+      const int ra = 4 * h + (Lg >> 2);
+      tr[db][0] = Swz<D>::off(ra, col >> 4) + (col & 15);
+      tr[db][1] = Swz<D>::off(ra + 8, col >> 4) + (col & 15);
+    }
+  }
+};
+
+// tile_row / tile_tr with precomputed offsets; r16 (a multiple of 16) is the row offset.
+template <int D>
+__device__ __forceinline__ bf16x8 tile_row_at(const char* tile, const LaneOffsets<D>& lo, int r16,
+                                              int dk) {
+  return lds_read_b128(tile + lo.row[dk] + r16 * Swz<D>::ROW);
+}
+template <int D>
+__device__ __forceinline__ bf16x8 tile_tr_at(const char* tile, const LaneOffsets<D>& lo, int r16,
+                                             int db) {
+  const bf16x4 x = lds_read_tr16(tile + lo.tr[db][0] + r16 * Swz<D>::ROW);
+  const bf16x4 y = lds_read_tr16(tile + lo.tr[db][1] + r16 * Swz<D>::ROW);
+  return __builtin_shufflevector(x, y, 0, 1, 2, 3, 4, 5, 6, 7);
+}
+
 // Row index (within a 32-row step) of accumulator register i of lane half h.
 __device__ __forceinline__ constexpr int acc_row(int i, int h) { return 8 * (i >> 2) + 4 * h + (i & 3); }
 
