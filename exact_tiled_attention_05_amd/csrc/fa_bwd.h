@@ -30,6 +30,8 @@
 // global-to-LDS loads of fa_tiles.h.
 #pragma once
 
+#include <type_traits>
+
 #include "fa_tiles.h"
 
 namespace fa {
@@ -125,24 +127,28 @@ __global__ __launch_bounds__(kBwdQWaves * 64) __attribute__((amdgpu_waves_per_eu
   dma_tile<D, kBwdTile, W>(sV2[0], vh, rs, 0, N, wave, lane);
   wait_dma();
   __syncthreads();
-  for (int j = 0; j < n_kt; j++) {
+  LaneOffsets<D> lo_;
+  lo_.init(lane);
+  // the stage is a compile-time constant of each copy of the loop body (immediate LDS offsets)
+  auto tile = [&](auto stage_c, int j) {
+    constexpr int stg = decltype(stage_c)::value;
     if (j + 1 < n_kt) {
-      dma_tile<D, kBwdTile, W>(sK2[(j + 1) & 1], kh, rs, (j + 1) * kBwdTile, N, wave, lane);
-      dma_tile<D, kBwdTile, W>(sV2[(j + 1) & 1], vh, rs, (j + 1) * kBwdTile, N, wave, lane);
+      dma_tile<D, kBwdTile, W>(sK2[stg ^ 1], kh, rs, (j + 1) * kBwdTile, N, wave, lane);
+      dma_tile<D, kBwdTile, W>(sV2[stg ^ 1], vh, rs, (j + 1) * kBwdTile, N, wave, lane);
     }
-    const char* sK = sK2[j & 1];
-    const char* sV = sV2[j & 1];
+    const char* sK = sK2[stg];
+    const char* sV = sV2[stg];
 #pragma unroll
     for (int sb = 0; sb < 2; sb++) {
       const int k0 = j * kBwdTile + 32 * sb;
-      if (k0 > wave_last) continue;
+      if (k0 > wave_last) continue;  // (next sb)
       f32x16 st = f32x16{}, dpt = f32x16{};
 #pragma unroll
       for (int dk = 0; dk < DK; dk++)
-        st = __builtin_amdgcn_mfma_f32_32x32x16_bf16(tile_row<D>(sK, 32 * sb + c, dk, h), qf[dk], st, 0, 0, 0);
+        st = __builtin_amdgcn_mfma_f32_32x32x16_bf16(tile_row_at<D>(sK, lo_, 32 * sb, dk), qf[dk], st, 0, 0, 0);
 #pragma unroll
       for (int dk = 0; dk < DK; dk++)
-        dpt = __builtin_amdgcn_mfma_f32_32x32x16_bf16(tile_row<D>(sV, 32 * sb + c, dk, h), df[dk], dpt, 0, 0, 0);
+        dpt = __builtin_amdgcn_mfma_f32_32x32x16_bf16(tile_row_at<D>(sV, lo_, 32 * sb, dk), df[dk], dpt, 0, 0, 0);
       // P^T = exp(S^T scale - L), masked; dS^T = P^T (dP^T - D). Register i holds key
       // k0 + acc_row(i, h), visible iff acc_row(i, 0) <= lim (keys below N and, causal, <= qrow).
       const bool edge = (CAUSAL && k0 + 31 > qw0) || k0 + 31 >= N;  // wave-uniform
@@ -158,13 +164,17 @@ __global__ __launch_bounds__(kBwdQWaves * 64) __attribute__((amdgpu_waves_per_eu
       for (int ks = 0; ks < 2; ks++)
 #pragma unroll
         for (int db = 0; db < DB; db++)
-          acc[db] = __builtin_amdgcn_mfma_f32_32x32x16_bf16(tile_tr<D>(sK, 32 * sb + 16 * ks, db, lane),
+          acc[db] = __builtin_amdgcn_mfma_f32_32x32x16_bf16(tile_tr_at<D>(sK, lo_, 32 * sb + 16 * ks, db),
                                                             dsf[ks], acc[db], 0, 0, 0);
     }
     if (j + 1 < n_kt) {
       wait_dma();
       __syncthreads();
     }
+  };
+  for (int j = 0; j < n_kt; j += 2) {
+    tile(std::integral_constant<int, 0>{}, j);
+    if (j + 1 < n_kt) tile(std::integral_constant<int, 1>{}, j + 1);
   }
 
   if (qrow < N) {
@@ -257,17 +267,22 @@ __global__ __launch_bounds__(kBwdKvWaves * 64) __attribute__((amdgpu_waves_per_e
   wait_dma();
   publish_step(0);
   __syncthreads();
-  for (int s = 0; s < n_steps; s++) {
+  LaneOffsets<D> lo_;
+  lo_.init(lane);
+  const int vb_row = 32 * wave;  // this wave's V rows in sVb
+  // the stage is a compile-time constant of each copy of the loop body (immediate LDS offsets)
+  auto step = [&](auto stage_c, int s) {
+    constexpr int stg = decltype(stage_c)::value;
     const int t = t0 + s % (n_qt - t0);
     if (s + 1 < n_steps) issue_step(s + 1);
-    const char* sQ = sQ2[s & 1];
-    const char* sO = sO2[s & 1];
-    const float* sL = sL2[s & 1];
-    const float* sD = sD2[s & 1];
+    const char* sQ = sQ2[stg];
+    const char* sO = sO2[stg];
+    const float* sL = sL2[stg];
+    const float* sD = sD2[stg];
 #pragma unroll
     for (int sb = 0; sb < 2; sb++) {
       const int q0 = t * kBwdTile + 32 * sb;
-      if (q0 >= N || (CAUSAL && q0 + 31 < kw0)) continue;
+      if (q0 >= N || (CAUSAL && q0 + 31 < kw0)) continue;  // (next sb)
       // register i holds query q0 + acc_row(i, h): visible iff below N and (causal) >= krow, i.e.
       // lo <= acc_row(i, 0) <= hi
       const bool edge = (CAUSAL && q0 < kw0 + 31) || q0 + 31 >= N;  // wave-uniform
@@ -278,7 +293,7 @@ __global__ __launch_bounds__(kBwdKvWaves * 64) __attribute__((amdgpu_waves_per_e
       f32x16 sc = f32x16{};
 #pragma unroll
       for (int dk = 0; dk < DK; dk++)
-        sc = __builtin_amdgcn_mfma_f32_32x32x16_bf16(tile_row<D>(sQ, 32 * sb + c, dk, h), kf[dk], sc, 0, 0, 0);
+        sc = __builtin_amdgcn_mfma_f32_32x32x16_bf16(tile_row_at<D>(sQ, lo_, 32 * sb, dk), kf[dk], sc, 0, 0, 0);
       float p[16];
       bf16x8 pf[2];
 #pragma unroll
@@ -297,14 +312,14 @@ __global__ __launch_bounds__(kBwdKvWaves * 64) __attribute__((amdgpu_waves_per_e
       for (int ks = 0; ks < 2; ks++)
 #pragma unroll
         for (int db = 0; db < DB; db++)
-          accv[db] = __builtin_amdgcn_mfma_f32_32x32x16_bf16(tile_tr<D>(sO, 32 * sb + 16 * ks, db, lane),
+          accv[db] = __builtin_amdgcn_mfma_f32_32x32x16_bf16(tile_tr_at<D>(sO, lo_, 32 * sb + 16 * ks, db),
                                                              pf[ks], accv[db], 0, 0, 0);
       // dP = dO V^T, dS = P (dP - D), then dK^T += Q^T dS
       f32x16 dp = f32x16{};
 #pragma unroll
       for (int dk = 0; dk < DK; dk++)
-        dp = __builtin_amdgcn_mfma_f32_32x32x16_bf16(tile_row<D>(sO, 32 * sb + c, dk, h),
-                                                     tile_row<D>(sVb, 32 * wave + c, dk, h), dp, 0, 0, 0);
+        dp = __builtin_amdgcn_mfma_f32_32x32x16_bf16(tile_row_at<D>(sO, lo_, 32 * sb, dk),
+                                                     tile_row_at<D>(sVb, lo_, vb_row, dk), dp, 0, 0, 0);
       bf16x8 dsf[2];
 #pragma unroll
       for (int j4 = 0; j4 < 4; j4++) {
@@ -319,7 +334,7 @@ __global__ __launch_bounds__(kBwdKvWaves * 64) __attribute__((amdgpu_waves_per_e
       for (int ks = 0; ks < 2; ks++)
 #pragma unroll
         for (int db = 0; db < DB; db++)
-          acck[db] = __builtin_amdgcn_mfma_f32_32x32x16_bf16(tile_tr<D>(sQ, 32 * sb + 16 * ks, db, lane),
+          acck[db] = __builtin_amdgcn_mfma_f32_32x32x16_bf16(tile_tr_at<D>(sQ, lo_, 32 * sb + 16 * ks, db),
                                                              dsf[ks], acck[db], 0, 0, 0);
     }
     if (s + 1 < n_steps) {
@@ -327,6 +342,10 @@ __global__ __launch_bounds__(kBwdKvWaves * 64) __attribute__((amdgpu_waves_per_e
       publish_step(s + 1);
       __syncthreads();
     }
+  };
+  for (int s = 0; s < n_steps; s += 2) {
+    step(std::integral_constant<int, 0>{}, s);
+    if (s + 1 < n_steps) step(std::integral_constant<int, 1>{}, s + 1);
   }
 
   if (krow < N && a.hsplit > 1) {
