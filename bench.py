@@ -43,6 +43,44 @@ def parse():
     return ap.parse_args()
 
 
+def host_info():
+    """Cores available, CPU model and BLAS library of this host (for the cpu_baseline record)."""
+    info = {"cores_available": len(os.sched_getaffinity(0))}
+    try:
+        with open("/proc/cpuinfo") as f:
+            for line in f:
+                if line.startswith("model name"):
+                    info["cpu_model"] = line.split(":", 1)[1].strip()
+                    break
+    except OSError:
+        pass
+    try:
+        from threadpoolctl import threadpool_info
+        blas = [i for i in threadpool_info() if i.get("user_api") == "blas"]
+        if blas:
+            info["blas"] = "%s %s" % (blas[0].get("internal_api"), blas[0].get("version"))
+    except Exception:  # pragma: no cover
+        pass
+    return info
+
+
+def per_launch_ms(step, stream, n=20):
+    """Median and minimum of n individually event-timed launches, run after the timed region
+    (each one alone on the idle GPU, so they include no queueing behind other launches)."""
+    import torch
+    ts = []
+    for _ in range(n):
+        e0 = torch.cuda.Event(enable_timing=True)
+        e1 = torch.cuda.Event(enable_timing=True)
+        e0.record(stream)
+        step()
+        e1.record(stream)
+        e1.synchronize()
+        ts.append(e0.elapsed_time(e1))
+    ts.sort()
+    return {"median": round(ts[len(ts) // 2], 5), "min": round(ts[0], 5), "launches": n}
+
+
 def copy_calibration(nbytes, steps):
     """A plain device-to-device copy of known size: reads and writes nbytes per launch."""
     import torch
@@ -80,9 +118,9 @@ def cpu_baseline(q, k, v, scale, causal, w, n_heads, budget_s=15.0):
             break
     from exact_tiled_attention_05_amd.workloads import metric_flops
     flops = metric_flops(1, done, w["N"], w["d"], causal)
-    return {"value": flops / dt / 1e12, "unit": "TFLOP/s", "cores": threads, "kind": "oracle",
-            "sample": "%d of %d heads, every row (numpy float64, dense S and P), %.1f s"
-                      % (done, w["B"] * w["H"], dt)}
+    return dict({"value": flops / dt / 1e12, "unit": "TFLOP/s", "cores": threads, "kind": "oracle",
+                 "sample": "%d of %d heads, every row (numpy float64, dense S and P), %.1f s"
+                           % (done, w["B"] * w["H"], dt)}, **host_info())
 
 
 def bench_decode(args, w):
@@ -148,6 +186,7 @@ def bench_decode(args, w):
                      "frac": round(alg_gbs / 8000.0, 4), "traffic": recorded_traffic(args.workload),
                      "algorithmic_bytes": alg},
         "wall_s_timed_region": round(wall, 4),
+        "kernel_ms": per_launch_ms(step, stream),
     }
     if not args.no_cpu:
         try:
@@ -175,6 +214,7 @@ def bench_decode(args, w):
                                "cores": threads, "kind": "oracle",
                                "sample": "%d of %d (batch, head) pairs, numpy float64, %.1f s"
                                          % (done, B * H, dt)}
+        rec["cpu_baseline"].update(host_info())
     print(json.dumps(rec), flush=True)
 
 
@@ -243,6 +283,7 @@ def bench_variant(args, w):
                      "unit": "TFLOP/s", "frac": round(tflops / PEAK_BF16_TFLOPS, 4),
                      "traffic": recorded_traffic(args.workload)},
         "wall_s_timed_region": round(wall, 4),
+        "kernel_ms": per_launch_ms(step, stream),
     }
     if not args.no_cpu:
         try:
@@ -271,6 +312,7 @@ def bench_variant(args, w):
                                "kind": "oracle",
                                "sample": "%d of %d heads of batch 0, every row (numpy float64, "
                                          "dense S and P), %.1f s" % (done, B * H, dt)}
+        rec["cpu_baseline"].update(host_info())
     print(json.dumps(rec), flush=True)
 
 
@@ -336,6 +378,7 @@ def bench_backward(args, w):
                      "unit": "TFLOP/s", "frac": round(tflops / PEAK_BF16_TFLOPS, 4),
                      "traffic": recorded_traffic(args.workload)},
         "wall_s_timed_region": round(wall, 4),
+        "kernel_ms": per_launch_ms(step, stream),
     }
     if not args.no_cpu:
         try:
@@ -360,6 +403,7 @@ def bench_backward(args, w):
                                "kind": "oracle",
                                "sample": "%d of %d heads of batch 0, every row (numpy float64, "
                                          "dense S, P, dP, dS), %.1f s" % (done, B * H, dt)}
+        rec["cpu_baseline"].update(host_info())
     print(json.dumps(rec), flush=True)
 
 
@@ -480,6 +524,7 @@ def main():
                      "achieved": round(tflops, 2), "peak": peak, "unit": "TFLOP/s",
                      "frac": round(tflops / peak, 4), "traffic": recorded_traffic(args.workload)},
         "wall_s_timed_region": round(wall, 4),
+        "kernel_ms": per_launch_ms(step, stream),
     }
     if not args.no_cpu:
         n_heads = args.cpu_heads or w["B"] * w["H"]
