@@ -371,13 +371,13 @@ def forward_ext(q, k, v, scale=None, causal=False, layout="bhnd", window=(-1, -1
                 tuple(bias.shape[2:]) != (N, N) or bias.stride(3) != 1:
             raise ValueError("bias must broadcast to [B, H, N, N] and be contiguous in its last "
                              "dimension")
-        if bias.stride(2) % 4 or bias.data_ptr() % 8:
-            raise ValueError("bias rows must start 8-byte aligned: a row stride that is a multiple "
-                             "of 4 elements (pad the last dimension)")
+        if bias.data_ptr() % 16 or any(bias.stride(i) % 8 for i in range(3) if bias.shape[i] > 1):
+            raise ValueError("bias rows must start 16-byte aligned: strides that are multiples of "
+                             "8 elements (pad the last dimension)")
         bp = bias.data_ptr()
         bs = bias.stride(0) if bias.shape[0] > 1 else 0
         hs = bias.stride(1) if bias.shape[1] > 1 else 0
-        rs = bias.stride(2)
+        rs = bias.stride(2) if N > 1 else 8  # one row: its stride is never used
     if out is None:
         out = torch.empty_like(q)
     if lse is None:

@@ -127,7 +127,9 @@ int run_ext(const void* q, const void* k, const void* v, void* o, float* lse, in
   }
   if (bias) {
     if (bias_bs < 0 || bias_hs < 0 || bias_rs < N) return FA_ERR_INVALID_ARG;
-    if ((reinterpret_cast<uintptr_t>(bias) & 7) || (bias_rs & 3)) return FA_ERR_ALIGNMENT;
+    // 16-byte chunks of the bias rows go straight into LDS: every row starts 16-byte aligned
+    if ((reinterpret_cast<uintptr_t>(bias) & 15) || (bias_rs & 7) || (bias_bs & 7) || (bias_hs & 7))
+      return FA_ERR_ALIGNMENT;
     // one head's matrix is addressed with 32-bit byte offsets
     if (((int64_t)(N - 1) * bias_rs + N) * 2 >= ((int64_t)1 << 31)) return FA_ERR_UNSUPPORTED;
     const size_t bb = (size_t)(((int64_t)(B - 1) * bias_bs + (int64_t)(H - 1) * bias_hs +

@@ -15,7 +15,8 @@
 //
 // Structure: 4 waves x 32 query rows per workgroup (several workgroups per CU), queries outermost;
 // K/V tiles (32 keys; 64 for d = 64) go straight from memory into two swizzled LDS stages
-// (fa_tiles.h), one barrier per tile. Per 32-key step a wave forms S^T = K Q^T (keys on M, so a
+// (fa_tiles.h), one barrier per tile; so does the bias tile of the workgroup's rows, one tile
+// ahead, so that its memory latency hides behind a whole tile of work. Per 32-key step a wave forms S^T = K Q^T (keys on M, so a
 // lane holds 16 keys of one query row), adds the bias and ALiBi terms in fp32, masks, moves the
 // running reference lazily (as the main kernel does; with the -inf reference guard of "Online
 // Softmax & FlashAttention", Listing 26.3), and accumulates O^T += V^T P^T with P rounded to bf16. A row that sees no key at
@@ -51,6 +52,28 @@ struct ExtTile {
   static constexpr int ROWS = D == 64 ? 64 : 32;
 };
 
+// Bias tile in LDS: the workgroup's 128 query rows x 64 keys (bf16, 128-byte rows), i.e. one or two
+// K/V tiles, filled by DMA in two stages. Each tile is requested as soon as its stage is free --
+// a whole bias tile ahead, up to two K/V tiles -- because the bias is read once from HBM, with no
+// L2 reuse to shorten the latency. A step reads 8 bytes per lane (4 keys of its row) and the LDS
+// serves such reads 32 lanes (one row each) at a time; chunk j of row R sits at slot j ^ g(R),
+// which spreads those 32 rows over all 16 (bank line half, slot) pairs: 2 rows per bank pair, the
+// least 32 rows of 8 bytes allow.
+struct BiasTile {
+  static constexpr int KEYS = 64;
+  static constexpr int ROW = 2 * KEYS;    // bytes per row
+  static constexpr int CPR = KEYS / 8;    // 16-byte chunks per row
+  static constexpr int RPP = 1024 / ROW;  // rows per 1 KB DMA piece
+  static constexpr int BYTES = kExtRows * ROW;
+  static constexpr int PIECES = BYTES / 1024;
+  static constexpr int PER_WAVE = PIECES / kExtWaves;
+  __device__ static __forceinline__ int g(int r) { return (r >> 1) & (CPR - 1); }
+};
+
+__device__ __forceinline__ bf16x4 lds_read_b64(const char* p) {
+  return *(const FA_LDS bf16x4*)(p);
+}
+
 struct ExtArgs {
   const bf16* q;
   const bf16* k;
@@ -75,6 +98,9 @@ __global__ __launch_bounds__(kExtWaves * 64) __attribute__((amdgpu_waves_per_eu(
   using S = Swz<D>;
   __shared__ __attribute__((aligned(1024))) char sK2[2][S::template bytes<TK>()];
   __shared__ __attribute__((aligned(1024))) char sV2[2][S::template bytes<TK>()];
+  using BT = BiasTile;
+  constexpr int TPB = BT::KEYS / TK;  // K/V tiles per bias tile
+  __shared__ __attribute__((aligned(1024))) char sB2[2][BIAS ? BT::BYTES : 16];
 
   const int tid = threadIdx.x, lane = tid & 63;
   const int wave = __builtin_amdgcn_readfirstlane(tid >> 6);
@@ -107,20 +133,36 @@ __global__ __launch_bounds__(kExtWaves * 64) __attribute__((amdgpu_waves_per_eu(
   lo_.init(lane);
   float slope2 = 0.f;
   if constexpr (ALIBI) slope2 = a.slopes[hq] * kLog2e;
-  // bias row of this lane's query (buffer resource over this head's matrix: rows past N and the
-  // columns past the last row's end read as zeros; columns past N are masked anyway)
-  __amdgpu_buffer_rsrc_t brs;
+  // Bias: a buffer resource over rows bq0.. of this head's matrix (bytes past row N-1's key N-1
+  // read as zeros), this lane's byte offset for each of its wave's DMA pieces (rows past N: an
+  // offset past the resource), and the LDS offsets of its reads (row 32 wave + c, chunk j, keys
+  // 4h..4h+3 of the chunk). Keys past N within a row are read but masked.
+  i32x4v brs;
+  unsigned bvo[BIAS ? BT::PER_WAVE : 1];
+  int boff[BIAS ? BT::CPR : 1];
   if constexpr (BIAS) {
-    const bf16* bh0 = a.bias + b * a.bias_bs + hq * a.bias_hs;
-    brs = __builtin_amdgcn_make_buffer_rsrc((void*)bh0, 0,
-                                            (int)(((long long)(N - 1) * a.bias_rs + N) * 2),
-                                            0x00020000);
-  }
-  auto load_bias = [&](int k0, bf16x4 (&bv)[4]) {
+    const long long rsb = 2LL * a.bias_rs;
+    const unsigned long long base = reinterpret_cast<unsigned long long>(
+        a.bias + b * a.bias_bs + hq * a.bias_hs) + (unsigned long long)(bq0 * rsb);
+    brs[0] = __builtin_amdgcn_readfirstlane((int)(base & 0xffffffffu));
+    brs[1] = __builtin_amdgcn_readfirstlane((int)(base >> 32));
+    brs[2] = __builtin_amdgcn_readfirstlane((int)(((long long)(N - 1 - bq0) * a.bias_rs + N) * 2));
+    brs[3] = 0x00020000;
+    const int rin = lane / BT::CPR, slot = lane % BT::CPR;
 #pragma unroll
-    for (int j4 = 0; j4 < 4; j4++)
-      bv[j4] = __builtin_bit_cast(bf16x4, __builtin_amdgcn_raw_buffer_load_b64(
-                   brs, (int)(((long long)qrow * a.bias_rs + k0 + 8 * j4 + 4 * h) * 2), 0, 0));
+    for (int i = 0; i < BT::PER_WAVE; i++) {
+      const int R = BT::RPP * (wave + kExtWaves * i) + rin;
+      bvo[i] = bq0 + R < N ? (unsigned)(R * rsb) + 16u * (unsigned)(slot ^ BT::g(R)) : 0x80000000u;
+    }
+    const int R = 32 * wave + c;
+#pragma unroll
+    for (int j = 0; j < BT::CPR; j++) boff[j] = R * BT::ROW + 16 * (j ^ BT::g(R)) + 8 * h;
+  }
+  auto dma_bias = [&](char* tile, int k0) {
+    const unsigned soff = __builtin_amdgcn_readfirstlane(2 * k0);
+#pragma unroll
+    for (int i = 0; i < BT::PER_WAVE; i++)
+      dma16(tile + 1024 * (wave + kExtWaves * i), bvo[i], brs, soff);
   };
 
   f32x16 acc[DB];
@@ -134,6 +176,7 @@ __global__ __launch_bounds__(kExtWaves * 64) __attribute__((amdgpu_waves_per_eu(
   if (t_first <= t_last) {
     dma_tile<D, TK, kExtWaves>(sK2[0], kh, rs, t_first * TK, N, wave, lane);
     dma_tile<D, TK, kExtWaves>(sV2[0], vh, rs, t_first * TK, N, wave, lane);
+    if constexpr (BIAS) dma_bias(sB2[0], t_first * TK);
     wait_dma();
     __syncthreads();
   }
@@ -145,15 +188,31 @@ __global__ __launch_bounds__(kExtWaves * 64) __attribute__((amdgpu_waves_per_eu(
       dma_tile<D, TK, kExtWaves>(sK2[st ^ 1], kh, rs, (t + 1) * TK, N, wave, lane);
       dma_tile<D, TK, kExtWaves>(sV2[st ^ 1], vh, rs, (t + 1) * TK, N, wave, lane);
     }
+    // bias tile of K/V tiles t.. (if t starts one): stage bst; its first tile requests the next
+    // bias tile into the other stage, after K/V so that the wait below can leave it in flight
+    const int bst = ((t - t_first) / TPB) & 1;
+    constexpr bool bias_first = TPB == 1 || st == 0;
+    bool bias_issued = false;
+    if constexpr (BIAS && bias_first) {
+      if (t + TPB <= t_last) {
+        dma_bias(sB2[bst ^ 1], (t + TPB) * TK);
+        bias_issued = true;
+      }
+    }
     const char* sK = sK2[st];
     const char* sV = sV2[st];
+    const char* sB = sB2[bst];
+    constexpr int bkey0 = TPB == 1 ? 0 : st * TK;  // this tile's first key within the bias tile
 #pragma unroll
     for (int sb = 0; sb < TK / 32; sb++) {
       const int k0 = t * TK + 32 * sb;
       // wave-uniform: no key of this step is visible to any row of the wave
       if (wq0 >= N || k0 > whi || k0 + 31 < wlo) continue;  // (continue: next sb)
       bf16x4 bcur[4];
-      if constexpr (BIAS) load_bias(k0, bcur);  // in flight during the QK products
+      if constexpr (BIAS) {
+#pragma unroll
+        for (int j4 = 0; j4 < 4; j4++) bcur[j4] = lds_read_b64(sB + boff[bkey0 / 8 + 4 * sb + j4]);
+      }
       f32x16 sc = f32x16{};
 #pragma unroll
       for (int dk = 0; dk < DK; dk++)
@@ -223,7 +282,12 @@ __global__ __launch_bounds__(kExtWaves * 64) __attribute__((amdgpu_waves_per_eu(
                                                             pf[ks], acc[db], 0, 0, 0);
     }
     if (t < t_last) {
-      wait_dma();
+      // K/V of tile t + 1 are the oldest loads in flight; a bias tile requested in this tile may
+      // stay in flight until the end of the next one (TPB = 2), by which its first tile is due
+      if (TPB == 2 && bias_issued)
+        wait_dma_but<BT::PER_WAVE>();
+      else
+        wait_dma();
       __syncthreads();
     }
   };

@@ -56,13 +56,21 @@ __device__ __forceinline__ i32x4v tile_rsrc(const char* head, long long rs, int 
   return r;
 }
 
-// Global memory -> LDS without registers: one 16-byte buffer load per lane whose data the
-// hardware writes at (M0 + 16 * lane), i.e. 1 KB per wave instruction (rows 4p..4p+3 of the
+// Global memory -> LDS without registers: one 16-byte buffer load per lane (voff + soff bytes into
+// the resource) whose data the hardware writes at (piece + 16 * lane), 1 KB per wave instruction.
+// dma_piece: piece p of a tile (rows 4p..4p+3 of the
 // swizzled tile for d = 128, 8p..8p+7 for d = 64, at LDS offset 1 KB * p). Lane l fills tile
 // position (row, slot) = (RPP p + l / CPR, l % CPR), so it fetches chunk slot ^ f(row) of that
 // row. The load counts on vmcnt; the caller waits for it before the barrier that publishes the
 // tile. (The DMA form is written as inline assembly: the compiler would otherwise wait for it
 // before every LDS access.)
+__device__ __forceinline__ void dma16(char* piece, unsigned voff, const i32x4v& rsrc,
+                                      unsigned soff) {
+  const unsigned m0 = __builtin_amdgcn_readfirstlane((int)(unsigned)(size_t)(FA_LDS char*)piece);
+  asm volatile("s_mov_b32 m0, %0\n\tbuffer_load_dwordx4 %1, %2, %3 offen lds"
+               :: "s"(m0), "v"(voff), "s"(rsrc), "s"(soff) : "memory", "m0");
+}
+
 template <int D>
 __device__ __forceinline__ void dma_piece(char* tile, const i32x4v& rsrc, long long rs, int p,
                                           int lane) {
@@ -70,10 +78,7 @@ __device__ __forceinline__ void dma_piece(char* tile, const i32x4v& rsrc, long l
   const int rin = lane / CPR, slot = lane % CPR;
   const unsigned voff = (unsigned)(rin * rs) + 16u * (unsigned)(slot ^ Swz<D>::f(RPP * p + rin));
   const unsigned soff = __builtin_amdgcn_readfirstlane((int)(RPP * p * rs));
-  const unsigned m0 = __builtin_amdgcn_readfirstlane(
-      (int)((unsigned)(size_t)(FA_LDS char*)tile + 1024u * (unsigned)p));
-  asm volatile("s_mov_b32 m0, %0\n\tbuffer_load_dwordx4 %1, %2, %3 offen lds"
-               :: "s"(m0), "v"(voff), "s"(rsrc), "s"(soff) : "memory", "m0");
+  dma16(tile + 1024 * p, voff, rsrc, soff);
 }
 
 // The ROWS-row tile of rows row0.. by W waves (tile bytes / 1 KB pieces, spread over the waves).
@@ -88,6 +93,12 @@ __device__ __forceinline__ void dma_tile(char* tile, const char* head, long long
 }
 
 __device__ __forceinline__ void wait_dma() { asm volatile("s_waitcnt vmcnt(0)" ::: "memory"); }
+// Wait for all but the N most recently issued loads (loads complete in issue order for vmcnt).
+template <int N>
+__device__ __forceinline__ void wait_dma_but() {
+  static_assert(N >= 0 && N < 64, "vmcnt range");
+  asm volatile("s_waitcnt vmcnt(%0)" :: "n"(N) : "memory");
+}
 
 // Row operand: 8 consecutive elements (chunk 2 dk + h) of tile row r.
 template <int D>

@@ -109,8 +109,9 @@ int fa_fwd_gqa_f32(const float* q, const float* k, const float* v, float* o, flo
  *   alibi_slopes: NULL or device fp32[H], slope m_h of query head h: the score gets - m_h |i - j|.
  *   bias: NULL or device bf16 matrix per (batch, query head): the score gets bias[b][h][i][j] at
  *       element offset b * bias_batch_stride + h * bias_head_stride + i * bias_row_stride + j;
- *       a stride of 0 shares the matrix across batches or heads; bias_row_stride >= N and a
- *       multiple of 4, the pointer 8-byte aligned (else FA_ERR_INVALID_ARG / FA_ERR_ALIGNMENT);
+ *       a stride of 0 shares the matrix across batches or heads; bias_row_stride >= N, all three
+ *       strides multiples of 8 and the pointer 16-byte aligned, so that every row starts 16-byte
+ *       aligned (else FA_ERR_INVALID_ARG / FA_ERR_ALIGNMENT);
  *       one head's matrix must span under 2 GiB (else FA_ERR_UNSUPPORTED). -inf entries mask.
  * The bias and ALiBi terms are added to the scaled score: S_ij = scale q_i.k_j + B_ij - m_h|i-j|.
  * A row with no visible key (only possible through -inf bias entries) gets O = 0 and

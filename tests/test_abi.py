@@ -294,8 +294,12 @@ BAD_EXT = [
     (dict(wr=-5), fa.FA_ERR_INVALID_ARG),
     (dict(d=96), fa.FA_ERR_UNSUPPORTED),
     (dict(brs=299), fa.FA_ERR_INVALID_ARG),          # rows shorter than N
-    (dict(brs=302), fa.FA_ERR_ALIGNMENT),             # row stride not a multiple of 4
+    (dict(brs=302), fa.FA_ERR_ALIGNMENT),             # row stride not a multiple of 8
+    (dict(brs=308), fa.FA_ERR_ALIGNMENT),
     (dict(bias=BI_ + 2), fa.FA_ERR_ALIGNMENT),
+    (dict(bias=BI_ + 8), fa.FA_ERR_ALIGNMENT),        # rows must start 16-byte aligned
+    (dict(bhs=300 * 304 + 4), fa.FA_ERR_ALIGNMENT),
+    (dict(bbs=12), fa.FA_ERR_ALIGNMENT),
     (dict(bhs=-1), fa.FA_ERR_INVALID_ARG),
     (dict(slopes=SL_ + 2), fa.FA_ERR_ALIGNMENT),
     (dict(N=40000, brs=40000, bhs=0), fa.FA_ERR_UNSUPPORTED),  # one matrix over 2 GiB

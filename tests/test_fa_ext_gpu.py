@@ -37,9 +37,9 @@ def gpu_ext(q, k, v, scale, causal, layout="bhnd", window=(-1, -1), slopes=None,
     qd, kd, vd = (to_layout(x, layout).to(DEV) for x in (q, k, v))
     sl = None if slopes is None else torch.tensor(slopes, device=DEV)
     bi = None
-    if bias is not None:  # rows padded to a multiple of 4 elements on the device (the contract)
+    if bias is not None:  # rows padded to a multiple of 8 elements on the device (the contract)
         n = bias.shape[-1]
-        pad = torch.zeros(tuple(bias.shape[:-1]) + ((n + 3) // 4 * 4,), dtype=torch.bfloat16,
+        pad = torch.zeros(tuple(bias.shape[:-1]) + ((n + 7) // 8 * 8,), dtype=torch.bfloat16,
                           device=DEV)
         pad[..., :n] = bias.to(DEV)
         bi = pad[..., :n]
