@@ -256,11 +256,13 @@ __global__ __launch_bounds__(kBwdKvWaves * 64) __attribute__((amdgpu_waves_per_e
     if (tid < 2 * kBwdTile) {
       const int r = t * kBwdTile + (tid & (kBwdTile - 1));
       const long long idx = (long long)bh * N + min(r, N - 1);
-      lsd = tid < kBwdTile ? a.lse[idx] * kLog2e : a.dsum[idx];
+      // raw value: any arithmetic on it here would make the compiler wait for the load at once,
+      // and with it (loads complete in order) for the DMA just issued
+      lsd = tid < kBwdTile ? a.lse[idx] : a.dsum[idx];
     }
   };
   auto publish_step = [&](int s) {  // after the DMA and the L/D loads of step s have landed
-    if (tid < kBwdTile) sL2[s & 1][tid] = lsd;
+    if (tid < kBwdTile) sL2[s & 1][tid] = lsd * kLog2e;
     else if (tid < 2 * kBwdTile) sD2[s & 1][tid - kBwdTile] = lsd;
   };
   issue_step(0);

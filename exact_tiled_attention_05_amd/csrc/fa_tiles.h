@@ -92,13 +92,20 @@ __device__ __forceinline__ void dma_tile(char* tile, const char* head, long long
   for (int i = 0; i < PIECES / W; i++) dma_piece<D>(tile, r, rs, wave + W * i, lane);
 }
 
-__device__ __forceinline__ void wait_dma() { asm volatile("s_waitcnt vmcnt(0)" ::: "memory"); }
+// The waits are the compiler's own s_waitcnt (not inline assembly), so that its wait insertion
+// knows the counter has drained: otherwise a load it issued before the loop (the Q operand)
+// stays pending in its books and it waits for vmcnt(0) -- including the DMA just issued for the
+// next tile -- at the first use inside the loop, on every iteration. The immediate holds vmcnt
+// in bits 3:0 and 15:14, expcnt in 6:4 and lgkmcnt in 11:8 (the last two left at their maxima).
+template <int N>
+__device__ __forceinline__ void wait_vmcnt() {
+  static_assert(N >= 0 && N < 64, "vmcnt range");
+  __builtin_amdgcn_s_waitcnt((N & 15) | ((N >> 4) << 14) | (7 << 4) | (15 << 8));
+}
+__device__ __forceinline__ void wait_dma() { wait_vmcnt<0>(); }
 // Wait for all but the N most recently issued loads (loads complete in issue order for vmcnt).
 template <int N>
-__device__ __forceinline__ void wait_dma_but() {
-  static_assert(N >= 0 && N < 64, "vmcnt range");
-  asm volatile("s_waitcnt vmcnt(%0)" :: "n"(N) : "memory");
-}
+__device__ __forceinline__ void wait_dma_but() { wait_vmcnt<N>(); }
 
 // Row operand: 8 consecutive elements (chunk 2 dk + h) of tile row r.
 template <int D>
