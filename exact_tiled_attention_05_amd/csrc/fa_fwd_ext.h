@@ -91,8 +91,12 @@ struct ExtArgs {
   int q_rs, kv_rs;
 };
 
+// Two waves per SIMD at least, d = 256 included: its 64 Q-operand and 128 accumulator registers
+// per lane fit in 256 VGPRs (with the halved lane offsets of fa_tiles.h), and the second wave is
+// what hides one wave's softmax behind the other's MFMAs (1.7x over one wave per SIMD). With a
+// bias the d = 256 kernel needs more and runs one wave per SIMD.
 template <int D, bool CAUSAL, bool ALIBI, bool BIAS>
-__global__ __launch_bounds__(kExtWaves * 64) __attribute__((amdgpu_waves_per_eu(D == 256 ? 1 : 2))) void fa_fwd_ext_kernel(ExtArgs a) {
+__global__ __launch_bounds__(kExtWaves * 64) __attribute__((amdgpu_waves_per_eu(2))) void fa_fwd_ext_kernel(ExtArgs a) {
   constexpr int DK = D / 16, DB = D / 32;
   constexpr int TK = ExtTile<D>::ROWS;
   using S = Swz<D>;

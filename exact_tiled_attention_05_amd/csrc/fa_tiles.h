@@ -127,17 +127,20 @@ __device__ __forceinline__ bf16x8 tile_tr(const char* tile, int r0, int db, int 
 
 // Per-lane byte offsets of those reads, computed once. The swizzle depends on the row only
 // through r mod 16, so a read at row offset 16 k (k a compile-time step index) is the lane's
-// offset plus the immediate 16 k * ROW: no address arithmetic in the loops.
+// offset plus the immediate 16 k * ROW: no address arithmetic in the loops. It permutes only the
+// low 4 bits of the chunk index, so the chunks of columns 128.. of a d = 256 row sit 256 bytes
+// past those of columns 0..127: offsets are kept for the first 128 columns only.
 template <int D>
 struct LaneOffsets {
-  int row[D / 16];     // row c, chunk 2 dk + h
-  int tr[D / 32][2];   // transposing reads of rows 4h + L/4 (and + 8) of a 16-row k-step, block db
+  static constexpr int DH = D > 128 ? 128 : D;
+  int row[DH / 16];     // row c, chunk 2 dk + h
+  int tr[DH / 32][2];   // transposing reads of rows 4h + L/4 (and + 8) of a 16-row k-step, block db
   __device__ __forceinline__ void init(int lane) {
     const int c = lane & 31, h = lane >> 5, Lg = lane & 15, hi = (lane >> 4) & 1;
 #pragma unroll
-    for (int dk = 0; dk < D / 16; dk++) row[dk] = Swz<D>::off(c, 2 * dk + h);
+    for (int dk = 0; dk < DH / 16; dk++) row[dk] = Swz<D>::off(c, 2 * dk + h);
 #pragma unroll
-    for (int db = 0; db < D / 32; db++) {
+    for (int db = 0; db < DH / 32; db++) {
       const int col = 64 * db + 32 * hi + 8 * (Lg & 3);
       const int ra = 4 * h + (Lg >> 2);
       tr[db][0] = Swz<D>::off(ra, col >> 4) + (col & 15);
@@ -150,13 +153,16 @@ struct LaneOffsets {
 template <int D>
 __device__ __forceinline__ bf16x8 tile_row_at(const char* tile, const LaneOffsets<D>& lo, int r16,
                                               int dk) {
-  return lds_read_b128(tile + lo.row[dk] + r16 * Swz<D>::ROW);
+  constexpr int NK = LaneOffsets<D>::DH / 16;
+  return lds_read_b128(tile + lo.row[dk % NK] + 256 * (dk / NK) + r16 * Swz<D>::ROW);
 }
 template <int D>
 __device__ __forceinline__ bf16x8 tile_tr_at(const char* tile, const LaneOffsets<D>& lo, int r16,
                                              int db) {
-  const bf16x4 x = lds_read_tr16(tile + lo.tr[db][0] + r16 * Swz<D>::ROW);
-  const bf16x4 y = lds_read_tr16(tile + lo.tr[db][1] + r16 * Swz<D>::ROW);
+  constexpr int NB = LaneOffsets<D>::DH / 32;
+  const int o = 256 * (db / NB) + r16 * Swz<D>::ROW;
+  const bf16x4 x = lds_read_tr16(tile + lo.tr[db % NB][0] + o);
+  const bf16x4 y = lds_read_tr16(tile + lo.tr[db % NB][1] + o);
   return __builtin_shufflevector(x, y, 0, 1, 2, 3, 4, 5, 6, 7);
 }
 
