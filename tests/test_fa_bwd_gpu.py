@@ -185,3 +185,29 @@ def test_backward_deterministic_and_workspace_reuse():
     b = gpu_fwd_bwd(q, k, v, do, 0.1, True, "bnhd", workspace=ws)
     for x, y in zip(a, b):
         assert np.array_equal(x, y)
+
+
+def test_backward_over_2g_elements_per_tensor():
+    # B=520, 32 query heads over 8 K/V heads, N=1024, d=128, causal, [B][N][H][d]: 2.2e9 elements
+    # per Q-sized tensor, so batch offsets need 64-bit arithmetic in every kernel. Inputs are drawn
+    # on the GPU; three batches are checked densely (every query head of one K/V group each).
+    B, H, H_kv, N, d = 520, 32, 8, 1024, 128
+    dev = DEV
+    log("bwd over 2^31 elements: B=%d H=%d H_kv=%d N=%d d=%d bnhd" % (B, H, H_kv, N, d))
+    g = torch.Generator(device=dev).manual_seed(993)
+    mk = lambda h: torch.randn((B, N, h, d), generator=g, device=dev).to(torch.bfloat16)
+    q, k, v, do = mk(H), mk(H_kv), mk(H_kv), mk(H)
+    assert q.numel() > 2 ** 31
+    scale = softmax_scale(d)
+    o, lse = fa.forward(q, k, v, scale=scale, causal=True, layout="bnhd")
+    dq, dk, dv = fa.backward(q, k, v, o, lse, do, scale=scale, causal=True, layout="bnhd")
+    torch.cuda.synchronize()
+    for b, j in [(0, 0), (B - 1, H_kv - 1), (263, 5)]:
+        cpu = lambda t: t[b:b + 1].permute(0, 2, 1, 3).contiguous().cpu()
+        qs, ks, vs, dos = cpu(q), cpu(k), cpu(v), cpu(do)
+        heads = [(0, h) for h in range(H) if kv_head_of(h, H, H_kv) == j]
+        ref, bnd = reference(qs, ks, vs, dos, scale, True, heads)
+        got = [cpu(t).float().numpy().astype(np.float64) for t in (dq, dk, dv)]
+        check(got, ref, bnd, "b=%d kv head %d" % (b, j))
+    del q, k, v, do, o, lse, dq, dk, dv
+    torch.cuda.empty_cache()

@@ -197,3 +197,33 @@ def test_error_codes():
     assert _raw_call(q, k, v, o, lse, B, H, H_kv, Nq, Nkv, d, scale=float("nan")) == \
         fa.FA_ERR_INVALID_ARG
     torch.cuda.synchronize()
+
+
+def test_decode_over_2g_elements_per_tensor():
+    # 64 sequences x 8 K/V heads x 65536 cached keys x d 128 in [B][N][H][d]: 4.3e9 elements
+    # (8.6 GB) per K/V tensor, so key offsets need 64-bit arithmetic. Drawn on the GPU; three
+    # (sequence, K/V head) groups checked against the oracle.
+    B, H, H_kv, Nq, N, d = 64, 32, 8, 1, 65536, 128
+    log("decode over 2^31 elements: B=%d H=%d H_kv=%d N_q=%d N_kv=%d d=%d bnhd" % (B, H, H_kv, Nq, N, d))
+    g = torch.Generator(device=DEV).manual_seed(994)
+    q = torch.randn((B, Nq, H, d), generator=g, device=DEV).to(torch.bfloat16)
+    k = torch.randn((B, N, H_kv, d), generator=g, device=DEV).to(torch.bfloat16)
+    v = torch.randn((B, N, H_kv, d), generator=g, device=DEV).to(torch.bfloat16)
+    assert k.numel() > 2 ** 31
+    scale = softmax_scale(d)
+    o, lse = fa.decode(q, k, v, scale=scale, causal=True, layout="bnhd")
+    torch.cuda.synchronize()
+    G = H // H_kv
+    for b, j in [(0, 0), (B - 1, H_kv - 1), (37, 3)]:
+        hs = slice(j * G, (j + 1) * G)
+        qs = q[b:b + 1, :, hs].permute(0, 2, 1, 3).cpu()
+        ks = k[b:b + 1, :, j:j + 1].permute(0, 2, 1, 3).cpu()
+        vs = v[b:b + 1, :, j:j + 1].permute(0, 2, 1, 3).cpu()
+        ro, rl = attention_decode(_as64(qs), _as64(ks), _as64(vs), scale, True)
+        go = o[b:b + 1, :, hs].permute(0, 2, 1, 3).float().cpu().numpy().astype(np.float64)
+        gl = lse[b:b + 1, hs].cpu().numpy().astype(np.float64)
+        eo, el = float(np.abs(go - ro).max()), float(np.abs(gl - rl).max())
+        log("  b=%d kv head %d: max|dO| %.3g  max|dLSE| %.3g" % (b, j, eo, el))
+        assert eo <= TOL_O_BF16 and el <= TOL_LSE
+    del q, k, v, o, lse
+    torch.cuda.empty_cache()

@@ -194,3 +194,33 @@ def test_bench_workloads_sampled_rows(name):
     rows = sampled_rows(w["N"], w["sample_rows"], seed=w["seed"]).numpy()
     check(q, k, v, scale, w["causal"][-1], w.get("layout", "bhnd"), tuple(w.get("window", (-1, -1))),
           slopes, bias, rows=rows, tag=name)
+
+
+def test_variants_over_2g_elements_per_tensor():
+    # B=20, 32 query heads over 8 K/V heads, N=32768, d=128, [B][N][H][d] (2.7e9 elements per Q),
+    # causal 4096-key window and ALiBi: the variant kernel's 64-bit offsets. Sampled rows of four
+    # heads checked.
+    from oracle import attention_head, kv_head_of
+    B, H, H_kv, N, d = 20, 32, 8, 32768, 128
+    log("ext over 2^31 elements: B=%d H=%d H_kv=%d N=%d d=%d bnhd window (4095, -1) alibi" % (B, H, H_kv, N, d))
+    g = torch.Generator(device=DEV).manual_seed(995)
+    mk = lambda h: torch.randn((B, N, h, d), generator=g, device=DEV).to(torch.bfloat16)
+    q, k, v = mk(H), mk(H_kv), mk(H_kv)
+    assert q.numel() > 2 ** 31
+    scale = softmax_scale(d)
+    sl = alibi(H)
+    o, lse = fa.forward_ext(q, k, v, scale=scale, causal=True, layout="bnhd", window=(4095, -1),
+                            alibi_slopes=torch.tensor(sl, device=DEV))
+    torch.cuda.synchronize()
+    rows = np.unique(np.concatenate([[0, 4095, 4096, N - 1], sampled_rows(N, 28, seed=996).numpy()]))
+    for b, h in [(0, 0), (B - 1, H - 1), (9, 14), (17, 3)]:
+        j = kv_head_of(h, H, H_kv)
+        ro, rl = attention_head(_as64(q[b, :, h].cpu()), _as64(k[b, :, j].cpu()), _as64(v[b, :, j].cpu()),
+                                scale, True, rows=rows, window=(4095, -1), alibi_slope=float(sl[h]))
+        go = o[b, :, h].float().cpu().numpy().astype(np.float64)[rows]
+        gl = lse[b, h].cpu().numpy().astype(np.float64)[rows]
+        eo, el = float(np.abs(go - ro).max()), float(np.abs(gl - rl).max())
+        log("  b=%d h=%d: max|dO| %.3g  max|dLSE| %.3g" % (b, h, eo, el))
+        assert eo <= TOL_O_BF16 and el <= TOL_LSE
+    del q, k, v, o, lse
+    torch.cuda.empty_cache()

@@ -271,3 +271,52 @@ def test_error_codes_on_device_tensors():
         assert fa.fa_fwd(*args, None) == code, args
     torch.cuda.synchronize()
     assert (o == 0).all() and (lse == 0).all()
+
+
+# --------------------------------------------------------------------------------------------
+# Tensors past 2^31 elements: every element offset needs 64-bit arithmetic.
+# --------------------------------------------------------------------------------------------
+
+def _big_inputs(B, H, H_kv, N, d, layout, seed):
+    """Seeded N(0, 1) bf16 Q, K, V drawn on the GPU (tensors this large would take minutes on the
+    host), in ``layout``."""
+    dev = torch.device("cuda:0")
+    g = torch.Generator(device=dev).manual_seed(seed)
+    shape = (lambda h: (B, h, N, d)) if layout == "bhnd" else (lambda h: (B, N, h, d))
+    return tuple(torch.randn(shape(h), generator=g, device=dev, dtype=torch.float32).to(torch.bfloat16)
+                 for h in (H, H_kv, H_kv))
+
+
+def _head(x, b, h, layout):
+    """One (b, h) slice [N, d] of a device tensor, as a CPU float64 array."""
+    t = x[b, h] if layout == "bhnd" else x[b, :, h]
+    return t.float().cpu().numpy().astype(np.float64)
+
+
+@pytest.mark.parametrize("layout", ["bhnd", "bnhd"])
+def test_over_2g_elements_per_tensor(layout):
+    # B=20, H=32, N=32768, d=128: 2.7e9 elements (5 GiB) per tensor, causal; grouped 32/8 heads in
+    # [B][N][H][d]. Heads in the first and last batch are checked on sampled rows.
+    from oracle import attention_head, kv_head_of
+    B, H, N, d = 20, 32, 32768, 128
+    H_kv = H if layout == "bhnd" else 8
+    log(f"[gpu] over 2^31 elements: B={B} H={H} H_kv={H_kv} N={N} d={d} layout={layout}")
+    q, k, v = _big_inputs(B, H, H_kv, N, d, layout, seed=991)
+    assert q.numel() > 2 ** 31
+    scale = W.softmax_scale(d)
+    o, lse = fa.forward(q, k, v, scale=scale, causal=True, layout=layout)
+    torch.cuda.synchronize()
+    rows = np.unique(np.concatenate([[0, 1, N - 1], W.sampled_rows(N, 29, seed=992).numpy()]))
+    worst_o = worst_l = 0.0
+    for b, h in [(0, 0), (B - 1, H - 1), (B - 1, 5), (11, 17)]:
+        j = kv_head_of(h, H, H_kv)
+        qh, kh, vh = _head(q, b, h, layout), _head(k, b, j, layout), _head(v, b, j, layout)
+        ro, rl = attention_head(qh, kh, vh, scale, True, rows=rows)
+        go = _head(o, b, h, layout)[rows]
+        gl = lse[b, h].cpu().numpy().astype(np.float64)[rows]
+        worst_o = max(worst_o, float(np.abs(go - ro).max()))
+        worst_l = max(worst_l, float(np.abs(gl - rl).max()))
+    log(f"[gpu] over 2^31 elements ({layout}): max|dO|={worst_o:.3e} max|dLSE|={worst_l:.3e}")
+    assert worst_o <= TOL_O_BF16 and worst_l <= TOL_LSE
+    del q, k, v, o, lse
+    torch.cuda.empty_cache()
