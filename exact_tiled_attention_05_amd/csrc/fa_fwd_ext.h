@@ -137,6 +137,24 @@ __global__ __launch_bounds__(kExtWaves * 64) __attribute__((amdgpu_waves_per_eu(
   lo_.init(lane);
   float slope2 = 0.f;
   if constexpr (ALIBI) slope2 = a.slopes[hq] * kLog2e;
+  // Causal ALiBi separates: every visible key has j <= i, so -m |i - j| = m (j - w0) - m (i - w0)
+  // (w0 the wave's first row). Register r of a step holds key k0 + acc_row(r, h), so in log2 units
+  // the score is fma(s, scale log2 e, C_r) + u with C_r = m log2(e) acc_row(r, 0) the same for
+  // every lane (scalar registers) and u = m log2(e) (k0 - w0 + 4h - c) one value per lane and step,
+  // which folds into the row maximum and the exponent's reference: one fma per score instead of
+  // a subtract, an absolute value and an fma. (Without the causal rule keys on both sides of the
+  // diagonal are visible and the absolute value stays; at d = 256 the 16 extra registers would
+  // spill.) Masked scores are -inf either way.
+  constexpr bool SEP = ALIBI && CAUSAL && D <= 128;
+  float alibi_c[SEP ? 16 : 1];
+  float alibi_lane = 0.f;
+  if constexpr (SEP) {
+#pragma unroll
+    for (int i = 0; i < 16; i++)
+      alibi_c[i] = __builtin_bit_cast(float, __builtin_amdgcn_readfirstlane(
+                       __builtin_bit_cast(int, slope2 * (float)acc_row(i, 0))));
+    alibi_lane = slope2 * (float)(4 * h - c);
+  }
   // Bias: a buffer resource over rows bq0.. of this head's matrix (bytes past row N-1's key N-1
   // read as zeros), this lane's byte offset for each of its wave's DMA pieces (rows past N: an
   // offset past the resource), and the LDS offsets of its reads (row 32 wave + c, chunk j, keys
@@ -228,6 +246,7 @@ __global__ __launch_bounds__(kExtWaves * 64) __attribute__((amdgpu_waves_per_eu(
       const int lo = qrow - a.wl - k0 - 4 * h;  // visible iff lo <= acc_row(i, 0) <= hi
       const int hi = min(N - 1, min(CAUSAL ? qrow : N - 1, qrow + a.wr)) - k0 - 4 * h;
       float t2;                   // this step's row maximum in log2 units (-inf: nothing visible)
+      float alibi_u = 0.f;        // SEP: the per-lane part of the ALiBi term (log2 units)
       float x[16];                // scores in log2 units, or raw scores (PLAIN)
       constexpr bool PLAIN = !ALIBI && !BIAS;
       if constexpr (PLAIN) {
@@ -242,13 +261,14 @@ __global__ __launch_bounds__(kExtWaves * 64) __attribute__((amdgpu_waves_per_eu(
         }
         t2 = half_swap_max(max16_arr(x)) * a.scale_log2;
       } else {
-        // x = scale log2(e) s + log2(e) (B - m |i - j|)
+        // x = scale log2(e) s + log2(e) (B - m |i - j|)   (SEP: minus u, see above)
         const float dq = (float)(qrow - k0 - 4 * h);  // qrow - key = dq - acc_row(i, 0)
+        if constexpr (SEP) alibi_u = __builtin_fmaf(slope2, (float)(k0 - wq0), alibi_lane);
 #pragma unroll
         for (int i = 0; i < 16; i++) {
-          float xi = sc[i] * a.scale_log2;
+          float xi = SEP ? __builtin_fmaf(sc[i], a.scale_log2, alibi_c[i]) : sc[i] * a.scale_log2;
           if constexpr (BIAS) xi = __builtin_fmaf((float)bcur[i >> 2][i & 3], kLog2e, xi);
-          if constexpr (ALIBI) xi = __builtin_fmaf(-slope2, __builtin_fabsf(dq - (float)acc_row(i, 0)), xi);
+          if constexpr (ALIBI && !SEP) xi = __builtin_fmaf(-slope2, __builtin_fabsf(dq - (float)acc_row(i, 0)), xi);
           x[i] = xi;
         }
         if (edge) {
@@ -256,7 +276,7 @@ __global__ __launch_bounds__(kExtWaves * 64) __attribute__((amdgpu_waves_per_eu(
           for (int i = 0; i < 16; i++)
             x[i] = (acc_row(i, 0) >= lo && acc_row(i, 0) <= hi) ? x[i] : -INFINITY;
         }
-        t2 = half_swap_max(max16_arr(x));
+        t2 = half_swap_max(max16_arr(x) + alibi_u);  // u differs between the row's two halves
       }
       // Running reference, moved only when a score exceeds it by more than kExtSlack (log2 units):
       // any reference gives the same softmax, and the accumulator rescale is skipped wave-wide
@@ -269,7 +289,7 @@ __global__ __launch_bounds__(kExtWaves * 64) __attribute__((amdgpu_waves_per_eu(
         for (int db = 0; db < DB; db++) acc[db] *= alpha;
         m2 = mn;
       }
-      const float ref = m2 == -INFINITY ? 0.f : m2;
+      const float ref = (m2 == -INFINITY ? 0.f : m2) - alibi_u;
       float p[16];
       bf16x8 pf[2];
 #pragma unroll

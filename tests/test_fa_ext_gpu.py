@@ -94,7 +94,9 @@ def test_sliding_window(N, H, H_kv, d, causal, layout, window):
 
 
 @pytest.mark.parametrize("N,d,causal,window", [(300, 128, True, (-1, -1)), (500, 64, False, (-1, -1)),
-                                               (1000, 128, True, (256, -1)), (257, 256, False, (40, 40))])
+                                               (1000, 128, True, (256, -1)), (257, 256, False, (40, 40)),
+                                               (333, 64, True, (-1, -1)), (700, 256, True, (100, -1)),
+                                               (129, 128, True, (0, 0))])
 def test_alibi(N, d, causal, window):
     H = 8
     q, k, v = make_inputs(2, H, N, d, H_kv=4, seed=N + d)
