@@ -407,15 +407,40 @@ def bench_backward(args, w):
     print(json.dumps(rec), flush=True)
 
 
-def kernel_source_digest():
-    """sha256 over the HIP sources and build flags of libfa.so (identifies the kernel build)."""
+# Sources that decide the code a workload runs: the C-ABI file (argument checks, launch shapes,
+# split and head-split plans), the header, the shared device helpers, and the kernel family.
+_FAMILY_SOURCES = {
+    "fwd": ("fa_fwd_bf16.h",),
+    "ext": ("fa_fwd_ext.h", "fa_tiles.h", "fa_fwd_bf16.h"),
+    "decode": ("fa_decode.h",),
+    "bwd": ("fa_bwd.h", "fa_tiles.h"),
+}
+
+
+def workload_family(workload):
+    from exact_tiled_attention_05_amd import workloads as W
+    w = W.WORKLOADS[workload]
+    if "Nq" in w:
+        return "decode"
+    if w.get("backward"):
+        return "bwd"
+    if w.get("window") or w.get("alibi") or w.get("bias_seed") or w["d"] == 256:
+        return "ext"
+    return "fwd"
+
+
+def kernel_source_digest(workload):
+    """sha256 over the build flags and the HIP sources of the kernels this workload runs (so a
+    change to another kernel family leaves its recorded counters valid)."""
     import hashlib
     from exact_tiled_attention_05_amd import build as B
     hsh = hashlib.sha256()
-    for d in (B.CSRC, B.INCLUDE):
-        for name in sorted(os.listdir(d)):
-            with open(os.path.join(d, name), "rb") as f:
-                hsh.update(name.encode() + b"\0" + f.read())
+    files = [os.path.join(B.CSRC, n) for n in
+             ("fa_api.hip", "fa_device.h") + _FAMILY_SOURCES[workload_family(workload)]]
+    files.append(os.path.join(B.INCLUDE, "fa.h"))
+    for path in files:
+        with open(path, "rb") as f:
+            hsh.update(os.path.basename(path).encode() + b"\0" + f.read())
     hsh.update(" ".join(B.HIP_FLAGS).encode())
     return hsh.hexdigest()
 
@@ -429,7 +454,7 @@ def recorded_traffic(workload):
             rec = json.load(f).get(workload)
     except (OSError, ValueError):
         return None
-    if not rec or rec.get("source_sha256") != kernel_source_digest():
+    if not rec or rec.get("source_sha256") != kernel_source_digest(workload):
         return None
     return rec.get("bytes_per_launch")
 
@@ -442,7 +467,7 @@ def main():
         sys.exit(2)
 
     if args.print_digest:
-        print(kernel_source_digest())
+        print(kernel_source_digest(args.workload))
         return
     if args.copy_calib:
         copy_calibration(args.copy_calib, args.steps)
