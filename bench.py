@@ -424,7 +424,9 @@ def workload_family(workload):
         return "decode"
     if w.get("backward"):
         return "bwd"
-    if w.get("window") or w.get("alibi") or w.get("bias_seed") or w["d"] == 256:
+    # the 4-wave kernel runs every variant, d = 256 and causal d = 128 bf16 (see fa_api.hip)
+    if (w.get("window") or w.get("alibi") or w.get("bias_seed") or w["d"] == 256
+            or (w["d"] == 128 and w["causal"][-1] and w["dtype"] == "bf16")):
         return "ext"
     return "fwd"
 
