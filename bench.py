@@ -424,9 +424,11 @@ def workload_family(workload):
         return "decode"
     if w.get("backward"):
         return "bwd"
-    # the 4-wave kernel runs every variant, d = 256 and causal d = 128 bf16 (see fa_api.hip)
+    # the 4-wave kernel runs every variant, d = 256, causal d = 128 and grids of more than 2^16
+    # query rows in bf16 (see fa_api.hip)
     if (w.get("window") or w.get("alibi") or w.get("bias_seed") or w["d"] == 256
-            or (w["d"] == 128 and w["causal"][-1] and w["dtype"] == "bf16")):
+            or (w["dtype"] == "bf16" and ((w["d"] == 128 and w["causal"][-1])
+                                          or w["B"] * w["H"] * w["N"] > (1 << 16)))):
         return "ext"
     return "fwd"
 

@@ -175,12 +175,14 @@ int run_ext(const void* q, const void* k, const void* v, void* o, float* lse, in
 
 int run_bf16(const void* q, const void* k, const void* v, void* o, float* lse, int B, int H,
              int H_kv, int N, int d, float scale, int causal, int layout, void* stream) {
-  // The 8-wave kernel runs d = 64 and non-causal d = 128; causal d = 128 and d = 256 run on the
-  // 4-wave kernel of the variants, with no variant enabled. On causal d = 128 the 4-wave kernel is
-  // 2.7-4.2% faster (one box, five alternating runs: the Llama layer with 32 and with 8 K/V heads,
-  // N = 32768), and 7-14% on shorter or smaller causal grids, whose imbalance its 128-row blocks
-  // even out; non-causal (N = 2048) and d = 64 the 8-wave kernel is 3-5% faster.
-  if (d == 256 || (d == 128 && causal == 1))
+  // Which forward kernel: the 4-wave kernel of the variants (no variant enabled) for d = 256, for
+  // causal d = 128 and for every grid of more than 2^16 query rows; the 8-wave kernel for the
+  // remaining small grids. Measured on one box (alternating runs): the 4-wave kernel is 2.7-4.2%
+  // faster on the causal Llama layer (32 and 8 K/V heads, N = 32768), 1-7% non-causal at d = 128
+  // (N 2048-32768, B up to 16), 5-20% at d = 64 on grids past 2^16 rows, and 14-21% on causal
+  // d = 128 grids as small as B=1 H=32 N=1024-2048, whose causal imbalance its 128-row blocks even
+  // out; on grids of at most 2^16 rows the 8-wave kernel is 3-5% faster non-causal and at d = 64.
+  if (d == 256 || (d == 128 && causal == 1) || (int64_t)B * H * N > (1 << 16))
     return run_ext(q, k, v, o, lse, B, H, H_kv, N, d, scale, causal, layout, -1, -1, nullptr,
                    nullptr, 0, 0, 0, stream);
   const int rc = check_args(q, k, v, o, lse, B, H, H_kv, N, d, scale, causal, layout, 2);
