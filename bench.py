@@ -433,9 +433,19 @@ def workload_family(workload):
     return "fwd"
 
 
+def _code_only(text):
+    """C++ source without comments and with whitespace runs collapsed (a comment edit leaves the
+    digest, and the counters keyed to it, unchanged)."""
+    import re
+    token = re.compile(r'"(?:\\.|[^"\\])*"|\'(?:\\.|[^\'\\])*\'|/\*.*?\*/|//[^\n]*', re.S)
+    text = token.sub(lambda m: m.group(0) if m.group(0)[0] in "\"'" else " ", text)
+    return " ".join(text.split())
+
+
 def kernel_source_digest(workload):
-    """sha256 over the build flags and the HIP sources of the kernels this workload runs (so a
-    change to another kernel family leaves its recorded counters valid)."""
+    """sha256 over the build flags and the code (comments stripped) of the HIP sources of the
+    kernels this workload runs (so a change to another kernel family leaves its recorded counters
+    valid)."""
     import hashlib
     from exact_tiled_attention_05_amd import build as B
     hsh = hashlib.sha256()
@@ -443,8 +453,8 @@ def kernel_source_digest(workload):
              ("fa_api.hip", "fa_device.h") + _FAMILY_SOURCES[workload_family(workload)]]
     files.append(os.path.join(B.INCLUDE, "fa.h"))
     for path in files:
-        with open(path, "rb") as f:
-            hsh.update(os.path.basename(path).encode() + b"\0" + f.read())
+        with open(path, encoding="utf-8") as f:
+            hsh.update(os.path.basename(path).encode() + b"\0" + _code_only(f.read()).encode())
     hsh.update(" ".join(B.HIP_FLAGS).encode())
     return hsh.hexdigest()
 

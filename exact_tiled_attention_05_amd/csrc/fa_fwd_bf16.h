@@ -1,4 +1,6 @@
-// bf16 attention forward kernel for gfx950: both contractions on bf16 MFMA, softmax in fp32.
+// 8-wave bf16 attention forward kernel for gfx950: both contractions on bf16 MFMA, softmax in
+// fp32. It runs the small grids (at most 2^16 query rows, non-causal or d = 64); the 4-wave kernel
+// of fa_fwd_ext.h runs the rest (the choice is made in fa_api.hip).
 //
 // The method ("FlashAttention-2 -- Deeper Math", Fixes 1-5 and "Causal masking: skip the blocks";
 // "Understanding FlashAttention Pt 1", §2.4 and §3.1): each workgroup owns a block of query rows

@@ -1,4 +1,6 @@
-// Forward kernel for the score variants and for d = 256, gfx950.
+// 4-wave forward kernel, gfx950: the score variants, d = 256, and (with no variant enabled) the
+// plain bf16 forward on causal d = 128 and on every grid past 2^16 query rows, where it is faster
+// than the 8-wave kernel (the choice and its measurements are in fa_api.hip).
 //
 // "Understanding FlashAttention Pt 1" writes the scores as S = QK^T / sqrt(d) + B, B an optional
 // additive mask or bias (§0.2), and lists local/sliding-window attention and ALiBi-style bias
@@ -6,7 +8,7 @@
 // "Flash Attention" put the supported head dims at 64, 128 and 256. This kernel computes
 //     S_ij = scale q_i.k_j + B_ij - m_h |i - j|,   key j visible iff causal rule and
 //            i - window_left <= j <= i + window_right,
-// with the same tiled online softmax as the main kernel: S and P stay in registers, a running
+// with the same tiled online softmax as the 8-wave kernel: S and P stay in registers, a running
 // maximum and sum per row, one division at the end, LSE = m + ln l. The bias B is a bf16 tensor
 // (any batch/head/row strides; stride 0 shares it), the ALiBi slopes m_h one fp32 per query head.
 // Tiles outside the window (or past the causal diagonal) are skipped for the whole workgroup, and
@@ -15,12 +17,13 @@
 //
 // Structure: 4 waves x 32 query rows per workgroup (several workgroups per CU), queries outermost;
 // K/V tiles (32 keys; 64 for d = 64) go straight from memory into two swizzled LDS stages
-// (fa_tiles.h), one barrier per tile; so does the bias tile of the workgroup's rows, one tile
-// ahead, so that its memory latency hides behind a whole tile of work. Per 32-key step a wave forms S^T = K Q^T (keys on M, so a
-// lane holds 16 keys of one query row), adds the bias and ALiBi terms in fp32, masks, moves the
-// running reference lazily (as the main kernel does; with the -inf reference guard of "Online
-// Softmax & FlashAttention", Listing 26.3), and accumulates O^T += V^T P^T with P rounded to bf16. A row that sees no key at
-// all (possible only through -inf bias entries) ends with O = 0 and LSE = -inf.
+// (fa_tiles.h), one barrier per tile; so do 64-key tiles of the bias for the workgroup's rows,
+// requested up to two K/V tiles ahead (BiasTile). Per 32-key step a wave forms S^T = K Q^T (keys
+// on M, so a lane holds 16 keys of one query row), adds the bias and ALiBi terms in fp32, masks,
+// moves the running reference lazily (as the 8-wave kernel does; with the -inf reference guard of
+// "Online Softmax & FlashAttention", Listing 26.3), and accumulates O^T += V^T P^T with P rounded
+// to bf16. A row that sees no key at all (possible only through -inf bias entries) ends with O = 0
+// and LSE = -inf.
 #pragma once
 
 #include <type_traits>
