@@ -16,7 +16,7 @@
 
 namespace {
 
-constexpr int kVersion = 500;  // 0.5.0: score variants (window, ALiBi, bias) and d = 256
+constexpr int kVersion = 600;  // 0.6.0: bias rows 16-byte aligned; forward kernel chosen by shape
 constexpr int kMaxN = 1 << 22;
 constexpr int kMaxBH = 65535;  // grid y of the fp32 kernel; also keeps bf16 grids < 2^31
 
