@@ -442,6 +442,18 @@ def _code_only(text):
     return " ".join(text.split())
 
 
+def device_kernel(workload):
+    """Name of the device kernel the forward entry point runs for this workload (fa_api.hip picks
+    it by shape)."""
+    from exact_tiled_attention_05_amd import workloads as W
+    w = W.WORKLOADS[workload]
+    if w["dtype"] != "bf16":
+        return "fa_fwd_f32_kernel"
+    if workload_family(workload) == "ext":
+        return "fa_fwd_ext_kernel, the 4-wave kernel"
+    return "fa_fwd_bf16_kernel, the 8-wave kernel"
+
+
 def kernel_source_digest(workload):
     """sha256 over the build flags and the code (comments stripped) of the HIP sources of the
     kernels this workload runs (so a change to another kernel family leaves its recorded counters
@@ -558,7 +570,7 @@ def main():
         "data": "synthetic (seeded N(0,1) Q, K, V)",
         "config": {"workload": args.workload, "B": w["B"], "H": w["H"], "H_kv": H_kv,
                    "N": w["N"], "d": w["d"], "causal": causal, "layout": layout,
-                   "kernel": fn.__name__},
+                   "kernel": "%s (%s)" % (fn.__name__, device_kernel(args.workload))},
         "roofline": {"bound": "mfma" if w["dtype"] == "bf16" else "alu",
                      "achieved": round(tflops, 2), "peak": peak, "unit": "TFLOP/s",
                      "frac": round(tflops / peak, 4), "traffic": recorded_traffic(args.workload)},
