@@ -1,0 +1,49 @@
+"""Host-side logic of bench.py (CPU): which kernel family and device kernel each workload runs, and
+the source digest that recorded HBM traffic is keyed to."""
+import json
+import os
+import sys
+
+ROOT = os.path.dirname(os.path.dirname(os.path.abspath(__file__)))
+sys.path.insert(0, ROOT)
+
+import bench  # noqa: E402
+from exact_tiled_attention_05_amd import workloads as W  # noqa: E402
+
+
+def test_family_follows_the_forward_kernel_choice():
+    # fa_api.hip: the 4-wave kernel for variants, d = 256, causal d = 128 and grids past 2^16 rows
+    assert bench.workload_family("llama3_8b_n8k_causal") == "ext"
+    assert bench.workload_family("llama3_8b_gqa_n8k_causal") == "ext"
+    assert bench.workload_family("outlier_b16h32_n2k") == "ext"        # 2^20 rows, non-causal
+    assert bench.workload_family("b4h16_n1k_d64") == "fwd"             # 2^16 rows, d = 64
+    assert bench.workload_family("single_head_fp32") == "fwd"
+    assert bench.workload_family("llama3_8b_gqa_decode_b8_n32k") == "decode"
+    assert bench.workload_family("llama3_8b_n8k_causal_bwd") == "bwd"
+    assert bench.workload_family("b1h16_n4k_bias") == "ext"
+    assert bench.device_kernel("single_head_fp32") == "fa_fwd_f32_kernel"
+    assert bench.device_kernel("b4h16_n1k_d64").startswith("fa_fwd_bf16_kernel")
+    assert bench.device_kernel("llama3_8b_n8k_causal").startswith("fa_fwd_ext_kernel")
+
+
+def test_code_only_drops_comments_but_not_strings():
+    src = 'int a; // note\n/* block\n comment */ int  b;\nconst char* s = "// kept \\" x"; char c = \'/\';'
+    assert bench._code_only(src) == 'int a; int b; const char* s = "// kept \\" x"; char c = \'/\';'
+    assert bench._code_only("x = 1; // a") == bench._code_only("x  =  1;   /* b */")
+
+
+def test_digest_is_per_family_and_stable():
+    d = {wl: bench.kernel_source_digest(wl) for wl in W.WORKLOADS}
+    assert all(len(x) == 64 for x in d.values())
+    assert d["llama3_8b_n8k_causal"] == d["d256_h16_n8k_causal"]        # same family, same sources
+    assert d["llama3_8b_n8k_causal"] != d["llama3_8b_n8k_causal_bwd"]
+    assert d["llama3_8b_gqa_decode_b8_n32k"] != d["llama3_8b_n8k_causal_bwd"]
+    assert bench.kernel_source_digest("llama3_8b_n8k_causal") == d["llama3_8b_n8k_causal"]
+
+
+def test_recorded_traffic_entries_are_well_formed():
+    with open(os.path.join(ROOT, "profiles", "traffic.json")) as f:
+        rec = json.load(f)
+    for wl, r in rec.items():
+        assert wl in W.WORKLOADS
+        assert len(r["source_sha256"]) == 64 and r["bytes_per_launch"] > 0
