@@ -67,7 +67,10 @@ __device__ __forceinline__ i32x4v tile_rsrc(const char* head, long long rs, int 
 __device__ __forceinline__ void dma16(char* piece, unsigned voff, const i32x4v& rsrc,
                                       unsigned soff) {
   const unsigned m0 = __builtin_amdgcn_readfirstlane((int)(unsigned)(size_t)(FA_LDS char*)piece);
-  asm volatile("s_mov_b32 m0, %0\n\tbuffer_load_dwordx4 %1, %2, %3 offen lds"
+  // s_nop 1: a VMEM instruction must not read an SGPR within two wait states of a VALU write to
+  // it (v_readfirstlane of the offsets), and the compiler's hazard recognizer does not look
+  // inside inline assembly; two wait states plus the s_mov cover it whatever precedes the block.
+  asm volatile("s_nop 1\n\ts_mov_b32 m0, %0\n\tbuffer_load_dwordx4 %1, %2, %3 offen lds"
                :: "s"(m0), "v"(voff), "s"(rsrc), "s"(soff) : "memory", "m0");
 }
 
