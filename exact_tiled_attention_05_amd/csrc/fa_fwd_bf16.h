@@ -171,25 +171,6 @@ struct Lane {
   float sl2;
 };
 
-// Tree reductions over the 16 values a lane holds for one 32x32 block (short dependency chains).
-__device__ __forceinline__ float max3(float a, float b, float c) {
-  return __builtin_fmaxf(__builtin_fmaxf(a, b), c);  // one v_max3_f32
-}
-__device__ __forceinline__ float max16(const f32x16& v) {
-  const float a = max3(v[0], v[1], v[2]), b = max3(v[3], v[4], v[5]);
-  const float c = max3(v[6], v[7], v[8]), d = max3(v[9], v[10], v[11]);
-  const float e = max3(v[12], v[13], v[14]);
-  return max3(max3(a, b, c), max3(d, e, v[15]), -INFINITY);
-}
-__device__ __forceinline__ float sum16(const float (&p)[16]) {
-  float t[8];
-#pragma unroll
-  for (int i = 0; i < 8; i++) t[i] = p[2 * i] + p[2 * i + 1];
-#pragma unroll
-  for (int i = 0; i < 4; i++) t[i] = t[2 * i] + t[2 * i + 1];
-  return (t[0] + t[1]) + (t[2] + t[3]);
-}
-
 // K operand of one 32-key step (sub-block sb of the tile at Kt).
 template <int D>
 __device__ __forceinline__ void read_k(const char* __restrict__ Kt, int sb, const Lane& L,
