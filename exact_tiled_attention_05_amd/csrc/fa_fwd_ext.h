@@ -102,6 +102,10 @@ template <int D, bool CAUSAL, bool ALIBI, bool BIAS>
 __global__ __launch_bounds__(kExtWaves * 64) __attribute__((amdgpu_waves_per_eu(2))) void fa_fwd_ext_kernel(ExtArgs a) {
   constexpr int DK = D / 16, DB = D / 32;
   constexpr int TK = ExtTile<D>::ROWS;
+  // K-operand reads in flight ahead of the score MFMAs: three for plain d = 128 (+0.7-1.3% on the
+  // causal and windowed Llama layers, the same 168 registers); none with ALiBi or a bias (the
+  // extra registers cost the third wave per SIMD) or at d = 64 and 256 (no measured gain).
+  constexpr int K_AHEAD = D == 128 && !ALIBI && !BIAS ? 3 : 0;
   using S = Swz<D>;
   __shared__ __attribute__((aligned(1024))) char sK2[2][S::template bytes<TK>()];
   __shared__ __attribute__((aligned(1024))) char sV2[2][S::template bytes<TK>()];
@@ -239,9 +243,26 @@ __global__ __launch_bounds__(kExtWaves * 64) __attribute__((amdgpu_waves_per_eu(
         for (int j4 = 0; j4 < 4; j4++) bcur[j4] = lds_read_b64(sB + boff[bkey0 / 8 + 4 * sb + j4]);
       }
       f32x16 sc = f32x16{};
+      if constexpr (K_AHEAD > 0) {
+        // K operands read K_AHEAD MFMAs ahead: reads first, then one read per MFMA, then the last
+        // MFMAs (left to itself the compiler waits for each read right before its MFMA)
+        bf16x8 kf[DK];
 #pragma unroll
-      for (int dk = 0; dk < DK; dk++)
-        sc = __builtin_amdgcn_mfma_f32_32x32x16_bf16(tile_row_at<D>(sK, lo_, 32 * sb, dk), qf[dk], sc, 0, 0, 0);
+        for (int dk = 0; dk < DK; dk++) kf[dk] = tile_row_at<D>(sK, lo_, 32 * sb, dk);
+#pragma unroll
+        for (int dk = 0; dk < DK; dk++) sc = __builtin_amdgcn_mfma_f32_32x32x16_bf16(kf[dk], qf[dk], sc, 0, 0, 0);
+        __builtin_amdgcn_sched_group_barrier(0x100, K_AHEAD, 0);  // LDS reads
+#pragma unroll
+        for (int i = 0; i < DK - K_AHEAD; i++) {
+          __builtin_amdgcn_sched_group_barrier(0x008, 1, 0);      // one MFMA
+          __builtin_amdgcn_sched_group_barrier(0x100, 1, 0);      // one LDS read
+        }
+        __builtin_amdgcn_sched_group_barrier(0x008, K_AHEAD, 0);
+      } else {
+#pragma unroll
+        for (int dk = 0; dk < DK; dk++)
+          sc = __builtin_amdgcn_mfma_f32_32x32x16_bf16(tile_row_at<D>(sK, lo_, 32 * sb, dk), qf[dk], sc, 0, 0, 0);
+      }
       // mask bounds: keys past N, past the causal diagonal or outside the window (only steps that
       // cross one of those bounds for some row of the wave); register i is key k0 + acc_row(i, h)
       const bool edge = k0 + 31 > min(N - 1, CAUSAL ? wq0 : N - 1) || k0 + 31 > wq0 + a.wr ||
