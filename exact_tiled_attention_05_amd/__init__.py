@@ -17,6 +17,8 @@ Raw entry points (same names and argument order as the C-ABI; pointers are integ
     fa_splitkv_workspace_bytes(B, H, H_kv, N_q, N_kv, d, causal, n_splits) -> int
     fa_fwd_splitkv(q, k, v, o, lse, B, H, H_kv, N_q, N_kv, d, scale, causal, layout, n_splits,
                    workspace, workspace_bytes, stream) -> int
+    fa_fwd_splitkv_noalloc(q, k, v, o, lse, B, H, H_kv, N_q, N_kv, d, scale, causal, layout,
+                           n_splits, stream) -> int
     fa_bwd_workspace_bytes(B, H, H_kv, N, d) -> int
     fa_bwd(q, k, v, o, dout, lse, dq, dk, dv, B, H, H_kv, N, d, scale, causal, layout, workspace,
            workspace_bytes, stream) -> int
@@ -37,17 +39,19 @@ import math
 import os
 
 __all__ = ["fa_fwd", "fa_fwd_f32", "fa_fwd_gqa", "fa_fwd_gqa_f32", "fa_fwd_ext", "forward_ext",
-           "fa_fwd_splitkv", "fa_bwd",
+           "fa_fwd_splitkv", "fa_fwd_splitkv_noalloc", "fa_bwd",
            "fa_bwd_workspace_bytes", "backward",
            "fa_splitkv_workspace_bytes", "fa_strerror", "fa_version", "forward", "decode", "FAError", "library_path", "load_library", "FA_OK", "FA_ERR_INVALID_ARG",
-           "FA_ERR_UNSUPPORTED", "FA_ERR_ALIGNMENT", "FA_ERR_LAUNCH", "FA_LAYOUT_BHND",
-           "FA_LAYOUT_BNHD"]
+           "FA_ERR_UNSUPPORTED", "FA_ERR_ALIGNMENT", "FA_ERR_LAUNCH", "FA_ERR_TOO_LARGE",
+           "FA_NOALLOC_SCRATCH_BYTES", "FA_LAYOUT_BHND", "FA_LAYOUT_BNHD"]
 
 FA_OK = 0
 FA_ERR_INVALID_ARG = -1
 FA_ERR_UNSUPPORTED = -2
 FA_ERR_ALIGNMENT = -3
 FA_ERR_LAUNCH = -4
+FA_ERR_TOO_LARGE = -5
+FA_NOALLOC_SCRATCH_BYTES = 16 << 20
 FA_LAYOUT_BHND = 0
 FA_LAYOUT_BNHD = 1
 
@@ -93,6 +97,10 @@ def load_library():
                                        [ctypes.c_float] + [ctypes.c_int] * 3 +
                                        [ctypes.c_void_p, ctypes.c_size_t, ctypes.c_void_p])
         lib.fa_fwd_splitkv.restype = ctypes.c_int
+        lib.fa_fwd_splitkv_noalloc.argtypes = ([ctypes.c_void_p] * 5 + [ctypes.c_int] * 6 +
+                                               [ctypes.c_float] + [ctypes.c_int] * 3 +
+                                               [ctypes.c_void_p])
+        lib.fa_fwd_splitkv_noalloc.restype = ctypes.c_int
         lib.fa_bwd_workspace_bytes.argtypes = [ctypes.c_int] * 5
         lib.fa_bwd_workspace_bytes.restype = ctypes.c_size_t
         lib.fa_bwd.argtypes = ([ctypes.c_void_p] * 9 + [ctypes.c_int] * 5 + [ctypes.c_float] +
@@ -141,6 +149,12 @@ def fa_fwd_splitkv(q, k, v, o, lse, B, H, H_kv, N_q, N_kv, d, scale, causal, lay
                    workspace, workspace_bytes, stream=None):
     return load_library().fa_fwd_splitkv(q, k, v, o, lse, B, H, H_kv, N_q, N_kv, d, scale, causal,
                                          layout, n_splits, workspace, workspace_bytes, stream)
+
+
+def fa_fwd_splitkv_noalloc(q, k, v, o, lse, B, H, H_kv, N_q, N_kv, d, scale, causal, layout,
+                           n_splits, stream=None):
+    return load_library().fa_fwd_splitkv_noalloc(q, k, v, o, lse, B, H, H_kv, N_q, N_kv, d, scale,
+                                                 causal, layout, n_splits, stream)
 
 
 def fa_bwd_workspace_bytes(B, H, H_kv, N, d):

@@ -6,6 +6,7 @@
 #include <cmath>
 #include <algorithm>
 #include <cstdint>
+#include <mutex>
 
 #include "fa.h"
 #include "fa_bwd.h"
@@ -279,6 +280,109 @@ hipError_t launch_decode(fa::DecodeArgs a, hipStream_t s) {
                          dim3(a.R, a.B_Hkv()), dim3(fa::kCombineThreads), args, 0, s);
 }
 
+// ---- the allocation-free split-KV entry point's scratch ---------------------------------------
+
+// Device memory for the split partials of fa_fwd_splitkv_noalloc, for callers that cannot
+// allocate. Each GPU the library runs on holds its own copy until the process ends; in host code
+// the name is only a stand-in, so kernels get the per-device address hipGetSymbolAddress returns.
+static __device__ __align__(256) unsigned char scratch[FA_NOALLOC_SCRATCH_BYTES];
+
+constexpr int kMaxDevices = 64;
+std::mutex g_scratch_mu;
+void* g_scratch_ptr[kMaxDevices] = {};
+
+// The scratch address on the device `stream` runs on, looked up once per device with that device
+// current (which the stream's device must be). FA_ERR_INVALID_ARG for a stream of another device.
+int static_scratch_address(hipStream_t stream, void** out) {
+  int dev = -1;
+  if (hipGetDevice(&dev) != hipSuccess || dev < 0 || dev >= kMaxDevices) return FA_ERR_LAUNCH;
+  if (stream) {
+    int sdev = -1;
+    if (hipStreamGetDevice(stream, &sdev) != hipSuccess) return FA_ERR_LAUNCH;
+    if (sdev != dev) return FA_ERR_INVALID_ARG;
+  }
+  std::lock_guard<std::mutex> lock(g_scratch_mu);
+  if (!g_scratch_ptr[dev]) {
+    void* p = nullptr;
+    if (hipGetSymbolAddress(&p, HIP_SYMBOL(scratch)) != hipSuccess || !p) return FA_ERR_LAUNCH;
+    g_scratch_ptr[dev] = p;
+  }
+  *out = g_scratch_ptr[dev];
+  return FA_OK;
+}
+
+// Shared by fa_fwd_splitkv (caller workspace) and fa_fwd_splitkv_noalloc (the library's static
+// scratch): checks, split plan, launches. ws = NULL asks for the static scratch, whose size is
+// checked right after the shape (before the pointers), and whose device address is looked up only
+// once every argument has passed.
+int run_splitkv(const void* q, const void* k, const void* v, void* o, float* lse, int B, int H,
+                int H_kv, int N_q, int N_kv, int d, float scale, int causal, int layout,
+                int n_splits, void* workspace, size_t workspace_bytes, bool static_scratch,
+                void* stream) {
+  if (!q || !k || !v || !o || !lse || (!static_scratch && !workspace)) return FA_ERR_INVALID_ARG;
+  int rc = check_decode_shape(B, H, H_kv, N_q, N_kv, d, causal, n_splits);
+  if (rc != FA_OK) return rc;
+  const SplitPlan sp = plan_splits(B, H_kv, N_kv, n_splits);
+  const int R = (H / H_kv) * N_q;
+  const size_t need = ws_bytes(B, H_kv, R, d, sp.n_splits);
+  if (static_scratch && need > FA_NOALLOC_SCRATCH_BYTES) return FA_ERR_TOO_LARGE;
+  if (layout != FA_LAYOUT_BHND && layout != FA_LAYOUT_BNHD) return FA_ERR_INVALID_ARG;
+  if (!std::isfinite(scale) || scale < 0.f) return FA_ERR_INVALID_ARG;
+  const uintptr_t mis = reinterpret_cast<uintptr_t>(q) | reinterpret_cast<uintptr_t>(k) |
+                        reinterpret_cast<uintptr_t>(v) | reinterpret_cast<uintptr_t>(o) |
+                        reinterpret_cast<uintptr_t>(lse) | reinterpret_cast<uintptr_t>(workspace);
+  if (mis & 15) return FA_ERR_ALIGNMENT;
+  if (!static_scratch && workspace_bytes < need) return FA_ERR_INVALID_ARG;
+  const size_t qb = (size_t)B * H * N_q * d * 2, kb = (size_t)B * H_kv * N_kv * d * 2;
+  const size_t lb = (size_t)B * H * N_q * sizeof(float);
+  const void* ins[3] = {q, k, v};
+  const size_t insz[3] = {qb, kb, kb};
+  for (int i = 0; i < 3; i++)
+    if (ranges_overlap(o, qb, ins[i], insz[i]) || ranges_overlap(lse, lb, ins[i], insz[i]) ||
+        (!static_scratch && ranges_overlap(workspace, need, ins[i], insz[i])))
+      return FA_ERR_INVALID_ARG;
+  if (ranges_overlap(o, qb, lse, lb) ||
+      (!static_scratch && (ranges_overlap(workspace, need, o, qb) ||
+                           ranges_overlap(workspace, need, lse, lb))))
+    return FA_ERR_INVALID_ARG;
+  const hipStream_t s = static_cast<hipStream_t>(stream);
+  if (static_scratch) {
+    rc = static_scratch_address(s, &workspace);
+    if (rc != FA_OK) return rc;
+  }
+
+  fa::DecodeArgs a;
+  a.q = static_cast<const fa::bf16*>(q);
+  a.k = static_cast<const fa::bf16*>(k);
+  a.v = static_cast<const fa::bf16*>(v);
+  a.o = static_cast<fa::bf16*>(o);
+  a.lse = lse;
+  a.ws_o = static_cast<float*>(workspace);
+  a.ws_lse = reinterpret_cast<float*>(static_cast<char*>(workspace) +
+                                      ws_lse_offset(B, H_kv, R, d, sp.n_splits));
+  a.Nq = N_q;
+  a.Nkv = N_kv;
+  a.H = H;
+  a.Hkv = H_kv;
+  a.group = H / H_kv;
+  a.B = B;
+  a.R = R;
+  a.n_splits = sp.n_splits;
+  a.keys_per_split = sp.keys_per_split;
+  a.causal = causal;
+  a.causal_off = N_kv - N_q;
+  a.scale_log2 = scale > 0.f ? scale * fa::kLog2e : FLT_MIN;
+  const Strides sq = strides_of(layout, H, N_q, d), sk = strides_of(layout, H_kv, N_kv, d);
+  a.q_bs = sq.bs;
+  a.q_hs = sq.hs;
+  a.q_rs = sq.rs;
+  a.kv_bs = sk.bs;
+  a.kv_hs = sk.hs;
+  a.kv_rs = sk.rs;
+  const hipError_t e = d == 128 ? launch_decode<128>(a, s) : launch_decode<64>(a, s);
+  return e == hipSuccess ? FA_OK : FA_ERR_LAUNCH;
+}
+
 // ---- backward ----------------------------------------------------------------------------------
 
 // Query-head splits of the dK/dV kernel: enough (K/V head, key block, split) workgroups for about
@@ -409,64 +513,16 @@ size_t fa_splitkv_workspace_bytes(int B, int H, int H_kv, int N_q, int N_kv, int
 int fa_fwd_splitkv(const void* q, const void* k, const void* v, void* o, float* lse, int B, int H,
                    int H_kv, int N_q, int N_kv, int d, float scale, int causal, int layout,
                    int n_splits, void* workspace, size_t workspace_bytes, void* stream) {
-  if (!q || !k || !v || !o || !lse || !workspace) return FA_ERR_INVALID_ARG;
-  int rc = check_decode_shape(B, H, H_kv, N_q, N_kv, d, causal, n_splits);
-  if (rc != FA_OK) return rc;
-  if (layout != FA_LAYOUT_BHND && layout != FA_LAYOUT_BNHD) return FA_ERR_INVALID_ARG;
-  if (!std::isfinite(scale) || scale < 0.f) return FA_ERR_INVALID_ARG;
-  const uintptr_t mis = reinterpret_cast<uintptr_t>(q) | reinterpret_cast<uintptr_t>(k) |
-                        reinterpret_cast<uintptr_t>(v) | reinterpret_cast<uintptr_t>(o) |
-                        reinterpret_cast<uintptr_t>(lse) | reinterpret_cast<uintptr_t>(workspace);
-  if (mis & 15) return FA_ERR_ALIGNMENT;
-  const SplitPlan sp = plan_splits(B, H_kv, N_kv, n_splits);
-  const int R = (H / H_kv) * N_q;
-  const size_t need = ws_bytes(B, H_kv, R, d, sp.n_splits);
-  if (workspace_bytes < need) return FA_ERR_INVALID_ARG;
-  const size_t qb = (size_t)B * H * N_q * d * 2, kb = (size_t)B * H_kv * N_kv * d * 2;
-  const size_t lb = (size_t)B * H * N_q * sizeof(float);
-  const void* ins[3] = {q, k, v};
-  const size_t insz[3] = {qb, kb, kb};
-  for (int i = 0; i < 3; i++)
-    if (ranges_overlap(o, qb, ins[i], insz[i]) || ranges_overlap(lse, lb, ins[i], insz[i]) ||
-        ranges_overlap(workspace, need, ins[i], insz[i]))
-      return FA_ERR_INVALID_ARG;
-  if (ranges_overlap(o, qb, lse, lb) || ranges_overlap(workspace, need, o, qb) ||
-      ranges_overlap(workspace, need, lse, lb))
-    return FA_ERR_INVALID_ARG;
-
-  fa::DecodeArgs a;
-  a.q = static_cast<const fa::bf16*>(q);
-  a.k = static_cast<const fa::bf16*>(k);
-  a.v = static_cast<const fa::bf16*>(v);
-  a.o = static_cast<fa::bf16*>(o);
-  a.lse = lse;
-  a.ws_o = static_cast<float*>(workspace);
-  a.ws_lse = reinterpret_cast<float*>(static_cast<char*>(workspace) +
-                                      ws_lse_offset(B, H_kv, R, d, sp.n_splits));
-  a.Nq = N_q;
-  a.Nkv = N_kv;
-  a.H = H;
-  a.Hkv = H_kv;
-  a.group = H / H_kv;
-  a.B = B;
-  a.R = R;
-  a.n_splits = sp.n_splits;
-  a.keys_per_split = sp.keys_per_split;
-  a.causal = causal;
-  a.causal_off = N_kv - N_q;
-  a.scale_log2 = scale > 0.f ? scale * fa::kLog2e : FLT_MIN;
-  const Strides sq = strides_of(layout, H, N_q, d), sk = strides_of(layout, H_kv, N_kv, d);
-  a.q_bs = sq.bs;
-  a.q_hs = sq.hs;
-  a.q_rs = sq.rs;
-  a.kv_bs = sk.bs;
-  a.kv_hs = sk.hs;
-  a.kv_rs = sk.rs;
-  const hipStream_t s = static_cast<hipStream_t>(stream);
-  const hipError_t e = d == 128 ? launch_decode<128>(a, s) : launch_decode<64>(a, s);
-  return e == hipSuccess ? FA_OK : FA_ERR_LAUNCH;
+  return run_splitkv(q, k, v, o, lse, B, H, H_kv, N_q, N_kv, d, scale, causal, layout, n_splits,
+                     workspace, workspace_bytes, false, stream);
 }
 
+int fa_fwd_splitkv_noalloc(const void* q, const void* k, const void* v, void* o, float* lse, int B,
+                           int H, int H_kv, int N_q, int N_kv, int d, float scale, int causal,
+                           int layout, int n_splits, void* stream) {
+  return run_splitkv(q, k, v, o, lse, B, H, H_kv, N_q, N_kv, d, scale, causal, layout, n_splits,
+                     nullptr, 0, true, stream);
+}
 
 int fa_fwd(const void* q, const void* k, const void* v, void* o, float* lse, int B, int H, int N,
            int d, float scale, int causal, void* stream) {
@@ -498,12 +554,15 @@ const char* fa_strerror(int code) {
              "of H_kv, layout not 0/1, causal not 0/1, scale negative or not finite, or a "
              "workspace that is too small)";
     case FA_ERR_UNSUPPORTED:
-      return "unsupported shape (head dimension not 64 or 128, or more than 32 query rows per "
-             "K/V head in split-KV decoding)";
+      return "unsupported shape (head dimension not 64 or 128 -- or 256 on the bf16 forward "
+             "entry points --, or more than 32 query rows per K/V head in split-KV decoding)";
     case FA_ERR_ALIGNMENT:
       return "pointer not 16-byte aligned";
     case FA_ERR_LAUNCH:
-      return "kernel launch failed";
+      return "kernel launch failed (or a HIP runtime query it needed failed)";
+    case FA_ERR_TOO_LARGE:
+      return "shape too large for the static scratch of fa_fwd_splitkv_noalloc "
+             "(FA_NOALLOC_SCRATCH_BYTES); use fa_fwd_splitkv with a workspace";
     default:
       return "unknown error code";
   }

@@ -32,7 +32,8 @@
  *     as FA_ERR_LAUNCH (the launch call's own status).
  *   - Deterministic: the same inputs give bitwise-identical outputs run to run (no atomics, no
  *     cross-workgroup reductions).
- *   - Thread-safe: no global mutable state.
+ *   - Thread-safe: no global mutable state (the one exception, the per-device scratch of
+ *     fa_fwd_splitkv_noalloc, is described with that function).
  *   - Limits: 1 <= N <= 2^22 and 1 <= B*H <= 65535.
  *
  * Grouped K/V heads ("Understanding FlashAttention Pt 1", §4.1): fa_fwd_gqa and fa_fwd_gqa_f32
@@ -56,9 +57,17 @@ extern "C" {
 #define FA_OK 0
 #define FA_ERR_INVALID_ARG (-1) /* null pointer, B/H/N out of range, causal not 0/1, scale
                                    negative or not finite, or overlapping output buffers */
-#define FA_ERR_UNSUPPORTED (-2) /* head dim d not in {64, 128}; split-KV: over 32 rows per K/V head */
+#define FA_ERR_UNSUPPORTED (-2) /* head dim d not in {64, 128} (the bf16 forward entry points
+                                   fa_fwd, fa_fwd_gqa and fa_fwd_ext also take 256); split-KV:
+                                   over 32 rows per K/V head */
 #define FA_ERR_ALIGNMENT (-3)   /* a pointer is not 16-byte aligned */
-#define FA_ERR_LAUNCH (-4)      /* the kernel launch call returned an error */
+#define FA_ERR_LAUNCH (-4)      /* the kernel launch call (or a HIP runtime query) returned an
+                                   error */
+#define FA_ERR_TOO_LARGE (-5)   /* fa_fwd_splitkv_noalloc: the shape needs more than the static
+                                   scratch holds (FA_NOALLOC_SCRATCH_BYTES) */
+
+/* Bytes of device scratch the library holds per GPU for fa_fwd_splitkv_noalloc (16 MiB). */
+#define FA_NOALLOC_SCRATCH_BYTES 16777216
 
 #define FA_LAYOUT_BHND 0 /* [B][heads][N][d] */
 #define FA_LAYOUT_BNHD 1 /* [B][N][heads][d] */
@@ -153,6 +162,23 @@ int fa_fwd_splitkv(const void* q, const void* k, const void* v, void* o, float* 
                    int B, int H, int H_kv, int N_q, int N_kv, int d, float scale, int causal,
                    int layout, int n_splits, void* workspace, size_t workspace_bytes,
                    void* stream);
+
+/*
+ * fa_fwd_splitkv_noalloc -- fa_fwd_splitkv for callers that cannot allocate device memory (code
+ *   under HIP graph capture, tight serving loops, harnesses that forbid hipMalloc): the same
+ *   kernels, split plan, arguments (minus the workspace), result and return codes, with the split
+ *   partials kept in a scratch array that the library holds in device memory, FA_NOALLOC_SCRATCH_BYTES
+ *   per GPU for as long as the process lives. It calls no allocator. A shape whose partials
+ *   (fa_splitkv_workspace_bytes(...) bytes) exceed the scratch returns FA_ERR_TOO_LARGE before any
+ *   HIP call. The first call on a device looks the scratch's address up on that device (the
+ *   current one, which `stream`, if not NULL, must belong to: else FA_ERR_INVALID_ARG). Every call
+ *   on one GPU shares that GPU's scratch: calls that may overlap in time on one GPU (two streams,
+ *   two host threads) race and must be serialised by the caller. The scratch needs no clearing:
+ *   every partial a call reads was written by the same call.
+ */
+int fa_fwd_splitkv_noalloc(const void* q, const void* k, const void* v, void* o, float* lse,
+                           int B, int H, int H_kv, int N_q, int N_kv, int d, float scale,
+                           int causal, int layout, int n_splits, void* stream);
 
 /*
  * Backward pass by recomputation ("Understanding FlashAttention Pt 1", §3.6; "Online Softmax &

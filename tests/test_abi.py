@@ -28,7 +28,8 @@ def _codes():
 def test_header_declares_the_expected_entry_points():
     assert _declared() == ["fa_bwd", "fa_bwd_workspace_bytes", "fa_fwd", "fa_fwd_ext",
                            "fa_fwd_f32", "fa_fwd_gqa", "fa_fwd_gqa_f32", "fa_fwd_splitkv",
-                           "fa_splitkv_workspace_bytes", "fa_strerror", "fa_version"]
+                           "fa_fwd_splitkv_noalloc", "fa_splitkv_workspace_bytes", "fa_strerror",
+                           "fa_version"]
 
 
 def test_library_exports_every_declared_symbol():
@@ -44,7 +45,7 @@ def test_python_codes_match_header():
 
 def test_version_and_strerror():
     assert fa.fa_version() >= 100
-    for code in (0, -1, -2, -3, -4):
+    for code in (0, -1, -2, -3, -4, -5):
         assert fa.fa_strerror(code) and fa.fa_strerror(code) != "unknown error code"
     assert fa.fa_strerror(12345) == "unknown error code"
 
@@ -207,6 +208,38 @@ def test_splitkv_workspace_bytes():
     assert f(1, 8, 2, 9, 4096, 128, 1, 0) == 0          # 36 rows per K/V head: not accepted
     assert f(1, 8, 3, 1, 4096, 128, 1, 0) == 0          # uneven head groups
     assert f(1, 8, 2, 1, 40, 128, 1, 1000) == f(1, 8, 2, 1, 40, 128, 1, 2)  # at most 1 split / 32 keys
+
+
+def _call_dec_noalloc(**kw):
+    a = dict(GOOD_DEC, **kw)
+    return fa.fa_fwd_splitkv_noalloc(a["q"], a["k"], a["v"], a["o"], a["lse"], a["B"], a["H"],
+                                     a["H_kv"], a["Nq"], a["Nkv"], a["d"], a["scale"], a["causal"],
+                                     a["layout"], a["n_splits"], None)
+
+
+# The allocation-free entry point refuses what fa_fwd_splitkv refuses (its workspace arguments
+# aside), and a shape whose partials exceed the static scratch, before any HIP call.
+BAD_DEC_NOALLOC = [(kw, code) for kw, code in BAD_DEC if not set(kw) & {"ws", "ws_bytes"}] + [
+    # 256 x 8 K/V heads x 32 stacked rows: one split each already needs 34 MB of partials
+    (dict(B=256, H=8, H_kv=8, Nq=32, Nkv=64, n_splits=1), fa.FA_ERR_TOO_LARGE),
+    # the library's split plan for 8 x 8 K/V heads x 4 rows over 1M keys: 12 splits, 3.2 MB, fits;
+    # an explicit 1024 splits does not
+    (dict(B=8, H=32, H_kv=8, Nq=1, Nkv=1 << 20, n_splits=1024), fa.FA_ERR_TOO_LARGE),
+]
+
+
+@pytest.mark.parametrize("kw,code", BAD_DEC_NOALLOC, ids=[str(b[0]) for b in BAD_DEC_NOALLOC])
+def test_bad_splitkv_noalloc_arguments_are_refused(kw, code):
+    assert _call_dec_noalloc(**kw) == code
+
+
+def test_noalloc_scratch_limit_matches_workspace_query():
+    f = fa.fa_splitkv_workspace_bytes
+    assert fa.FA_NOALLOC_SCRATCH_BYTES == 16 << 20
+    assert f(256, 8, 8, 32, 64, 128, 1, 1) > fa.FA_NOALLOC_SCRATCH_BYTES
+    assert f(8, 32, 8, 1, 1 << 20, 128, 1, 1024) > fa.FA_NOALLOC_SCRATCH_BYTES
+    # the Llama-3-8B decoding batch (8 sequences, 32 query over 8 K/V heads, 32K keys) fits
+    assert 0 < f(8, 32, 8, 1, 32768, 128, 1, 0) <= fa.FA_NOALLOC_SCRATCH_BYTES
 
 
 # ---- backward ------------------------------------------------------------------------------------
