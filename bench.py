@@ -411,6 +411,7 @@ def bench_backward(args, w):
 # split and head-split plans), the header, the shared device helpers, and the kernel family.
 _FAMILY_SOURCES = {
     "fwd": ("fa_fwd_bf16.h",),
+    "wide": ("fa_fwd_wide.h", "fa_wide.hip", "fa_tiles.h"),
     "ext": ("fa_fwd_ext.h", "fa_tiles.h", "fa_fwd_bf16.h"),
     "decode": ("fa_decode.h",),
     "bwd": ("fa_bwd.h", "fa_tiles.h"),
@@ -424,11 +425,15 @@ def workload_family(workload):
         return "decode"
     if w.get("backward"):
         return "bwd"
-    # the 4-wave kernel runs every variant, d = 256, causal d = 128 and grids of more than 2^16
-    # query rows in bf16 (see fa_api.hip)
-    if (w.get("window") or w.get("alibi") or w.get("bias_seed") or w["d"] == 256
-            or (w["dtype"] == "bf16" and ((w["d"] == 128 and w["causal"][-1])
-                                          or w["B"] * w["H"] * w["N"] > (1 << 16)))):
+    # fa_api.hip: every variant runs the 4-wave kernel; plain bf16 d = 128 with N >= 4096 the
+    # wide-row kernel; d = 256, the rest of causal d = 128 and grids of more than 2^16 query rows
+    # the 4-wave kernel; the remaining small grids the 8-wave kernel
+    if w.get("window") or w.get("alibi") or w.get("bias_seed"):
+        return "ext"
+    if w["dtype"] == "bf16" and w["d"] == 128 and w["N"] >= 4096:
+        return "wide"
+    if (w["d"] == 256 or (w["dtype"] == "bf16" and ((w["d"] == 128 and w["causal"][-1])
+                                                    or w["B"] * w["H"] * w["N"] > (1 << 16)))):
         return "ext"
     return "fwd"
 
@@ -449,6 +454,8 @@ def device_kernel(workload):
     w = W.WORKLOADS[workload]
     if w["dtype"] != "bf16":
         return "fa_fwd_f32_kernel"
+    if workload_family(workload) == "wide":
+        return "fa_fwd_wide_kernel, the wide-row kernel"
     if workload_family(workload) == "ext":
         return "fa_fwd_ext_kernel, the 4-wave kernel"
     return "fa_fwd_bf16_kernel, the 8-wave kernel"

@@ -1,7 +1,8 @@
 """Build libfa.so (the C-ABI attention library) in-tree with hipcc for gfx950.
 
 Usage: ``python -m exact_tiled_attention_05_amd.build`` or ``build()`` from Python. The library
-lands next to this file, where the Python binding loads it from.
+lands next to this file, where the Python binding loads it from. Each translation unit is compiled
+to an object with its own flags, then the objects are linked into one shared library.
 """
 import os
 import subprocess
@@ -16,10 +17,19 @@ LIB_PATH = os.path.join(PKG_DIR, "libfa.so")
 # Packed fp32 VALU instructions are disabled for all device code. NaNs are never produced by the
 # kernels for finite inputs (hidden keys are -inf, never 0*inf), so max needs no NaN handling.
 HIP_FLAGS = [
-    "--offload-arch=gfx950", "-O3", "-std=c++17", "-fPIC", "-shared",
+    "--offload-arch=gfx950", "-O3", "-std=c++17", "-fPIC",
     "-Xclang", "-target-feature", "-Xclang", "-packed-fp32-ops",
     "-fno-honor-nans",
     "-Wall", "-Wno-unused-result",
+]
+
+# Translation units of the library and the extra flags of each. The wide-row forward kernel needs
+# about 360 registers per lane; with its MFMA results forced into VGPRs the Q operands go to AGPRs
+# (read directly by the MFMAs) instead of the accumulators the softmax reads and rescales. The
+# flag is kept to that file so that it changes no other kernel.
+SOURCES = [
+    ("fa_api.hip", []),
+    ("fa_wide.hip", ["-mllvm", "-amdgpu-mfma-vgpr-form"]),
 ]
 
 
@@ -27,11 +37,7 @@ def hipcc_path():
     return os.environ.get("HIPCC", "/opt/rocm/bin/hipcc")
 
 
-def build(verbose=False, extra_flags=(), out=LIB_PATH):
-    """Compile csrc/fa_api.hip (which includes the kernels) into ``out``; returns its path."""
-    tmp = out + ".tmp%d" % os.getpid()
-    cmd = [hipcc_path()] + HIP_FLAGS + list(extra_flags) + [
-        "-I", INCLUDE, "-I", CSRC, os.path.join(CSRC, "fa_api.hip"), "-o", tmp]
+def _run(cmd, verbose):
     if verbose:
         print(" ".join(cmd), flush=True)
     r = subprocess.run(cmd, stdout=subprocess.PIPE, stderr=subprocess.STDOUT, text=True)
@@ -41,7 +47,26 @@ def build(verbose=False, extra_flags=(), out=LIB_PATH):
         raise RuntimeError("hipcc failed (%d):\n%s" % (r.returncode, "\n".join(msgs)))
     if verbose and msgs:
         print("\n".join(msgs), flush=True)
-    os.replace(tmp, out)
+
+
+def build(verbose=False, extra_flags=(), out=LIB_PATH):
+    """Compile the library's translation units and link them into ``out``; returns its path."""
+    tag = "%d" % os.getpid()
+    objs = []
+    try:
+        for src, flags in SOURCES:
+            obj = os.path.join(os.path.dirname(out), "%s.%s.o" % (os.path.splitext(src)[0], tag))
+            _run([hipcc_path()] + HIP_FLAGS + flags + list(extra_flags) +
+                 ["-I", INCLUDE, "-I", CSRC, "-c", os.path.join(CSRC, src), "-o", obj], verbose)
+            objs.append(obj)
+        tmp = out + ".tmp" + tag
+        _run([hipcc_path(), "--offload-arch=gfx950", "-shared", "-fPIC"] + objs + ["-o", tmp],
+             verbose)
+        os.replace(tmp, out)
+    finally:
+        for obj in objs:
+            if os.path.exists(obj):
+                os.remove(obj)
     return out
 
 

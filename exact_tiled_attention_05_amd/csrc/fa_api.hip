@@ -14,6 +14,12 @@
 #include "fa_fwd_bf16.h"
 #include "fa_fwd_ext.h"
 #include "fa_fwd_f32.h"
+#include "fa_fwd_wide.h"
+
+namespace fa {
+// fa_wide.hip (compiled separately, see there)
+hipError_t launch_wide(const WideArgs& args, bool causal, hipStream_t stream);
+}  // namespace fa
 
 namespace {
 
@@ -174,8 +180,33 @@ int run_ext(const void* q, const void* k, const void* v, void* o, float* lse, in
   return e == hipSuccess ? FA_OK : FA_ERR_LAUNCH;
 }
 
+int run_wide(const void* q, const void* k, const void* v, void* o, float* lse, int B, int H,
+             int H_kv, int N, float scale, int causal, int layout, void* stream) {
+  const int rc = check_args(q, k, v, o, lse, B, H, H_kv, N, 128, scale, causal, layout, 2);
+  if (rc != FA_OK) return rc;
+  fa::WideArgs a;
+  a.q = static_cast<const fa::bf16*>(q);
+  a.k = static_cast<const fa::bf16*>(k);
+  a.v = static_cast<const fa::bf16*>(v);
+  a.o = static_cast<fa::bf16*>(o);
+  a.lse = lse;
+  fill_shape(a, B, H, H_kv, N, 128, layout);
+  a.scale_log2 = scale > 0.f ? scale * fa::kLog2e : FLT_MIN;
+  a.n_qblk = (N + fa::kWideRows - 1) / fa::kWideRows;
+  const hipStream_t s = static_cast<hipStream_t>(stream);
+  const hipError_t e = fa::launch_wide(a, causal == 1, s);
+  return e == hipSuccess ? FA_OK : FA_ERR_LAUNCH;
+}
+
 int run_bf16(const void* q, const void* k, const void* v, void* o, float* lse, int B, int H,
              int H_kv, int N, int d, float scale, int causal, int layout, void* stream) {
+  // d = 128 and N >= 4096: the wide-row kernel (fa_fwd_wide.h). Measured on one box against the
+  // 4-wave kernel, TFLOP/s: causal B=1 H=32 N=8192 1150 / 1080, N=32768 1205 / 1105, 8 K/V heads
+  // N=8192 1155 / 1082, N=4096 988 / 955; non-causal B=1 H=32 N=4096 1146 / 1024, B=4 H=16
+  // N=4096 1166 / 1070. Below N = 4096 its 256-row workgroups leave too few (and, causal, too
+  // unequal) blocks: causal N=2048 561 / 628, N=1024 251 / 322.
+  if (d == 128 && N >= 4096)
+    return run_wide(q, k, v, o, lse, B, H, H_kv, N, scale, causal, layout, stream);
   // Which forward kernel: the 4-wave kernel of the variants (no variant enabled) for d = 256, for
   // causal d = 128 and for every grid of more than 2^16 query rows; the 8-wave kernel for the
   // remaining small grids. Measured on one box (alternating runs): the 4-wave kernel is 2.7-4.2%

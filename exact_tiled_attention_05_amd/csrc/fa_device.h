@@ -49,6 +49,17 @@ __device__ __forceinline__ float max16(const f32x16& v) {
   const float e = max3(v[12], v[13], v[14]);
   return max3(max3(a, b, c), max3(d, e, v[15]), -INFINITY);
 }
+// The same maximum over 16 values held in an array (six v_max3_f32).
+__device__ __forceinline__ float max16_arr(const float (&v)[16]) {
+  float a = __builtin_fmaxf(__builtin_fmaxf(v[0], v[1]), v[2]);
+  float b = __builtin_fmaxf(__builtin_fmaxf(v[3], v[4]), v[5]);
+  float c = __builtin_fmaxf(__builtin_fmaxf(v[6], v[7]), v[8]);
+  float d = __builtin_fmaxf(__builtin_fmaxf(v[9], v[10]), v[11]);
+  float e = __builtin_fmaxf(__builtin_fmaxf(v[12], v[13]), v[14]);
+  return __builtin_fmaxf(__builtin_fmaxf(__builtin_fmaxf(a, b), c),
+                         __builtin_fmaxf(__builtin_fmaxf(d, e), v[15]));
+}
+
 __device__ __forceinline__ float sum16(const float (&p)[16]) {
   float t[8];
 #pragma unroll

@@ -37,16 +37,6 @@ constexpr int kExtRows = 32 * kExtWaves;  // query rows per workgroup
 constexpr int kExtNoWindow = 1 << 30;     // a window bound that never binds
 constexpr float kExtSlack = 2.f;          // lazy reference: moved when exceeded by > 2 (log2)
 
-__device__ __forceinline__ float max16_arr(const float (&v)[16]) {
-  float a = __builtin_fmaxf(__builtin_fmaxf(v[0], v[1]), v[2]);
-  float b = __builtin_fmaxf(__builtin_fmaxf(v[3], v[4]), v[5]);
-  float c = __builtin_fmaxf(__builtin_fmaxf(v[6], v[7]), v[8]);
-  float d = __builtin_fmaxf(__builtin_fmaxf(v[9], v[10]), v[11]);
-  float e = __builtin_fmaxf(__builtin_fmaxf(v[12], v[13]), v[14]);
-  return __builtin_fmaxf(__builtin_fmaxf(__builtin_fmaxf(a, b), c),
-                         __builtin_fmaxf(__builtin_fmaxf(d, e), v[15]));
-}
-
 // Keys per LDS tile: 32 for d = 128 and 256 (32 KB for both stages of K and V at d = 128, so three
 // workgroups share a CU), 64 for d = 64. On the causal Llama layer 32-key tiles ran at 1109 TFLOP/s
 // against 1063 for 64-key tiles (one box, round-robin).

@@ -12,18 +12,24 @@ from exact_tiled_attention_05_amd import workloads as W  # noqa: E402
 
 
 def test_family_follows_the_forward_kernel_choice():
-    # fa_api.hip: the 4-wave kernel for variants, d = 256, causal d = 128 and grids past 2^16 rows
-    assert bench.workload_family("llama3_8b_n8k_causal") == "ext"
-    assert bench.workload_family("llama3_8b_gqa_n8k_causal") == "ext"
-    assert bench.workload_family("outlier_b16h32_n2k") == "ext"        # 2^20 rows, non-causal
+    # fa_api.hip: the 4-wave kernel for every variant, the wide-row kernel for plain bf16 d = 128
+    # with N >= 4096, the 4-wave kernel for d = 256, the other causal d = 128 grids and grids past
+    # 2^16 rows, the 8-wave kernel for the rest
+    assert bench.workload_family("llama3_8b_n8k_causal") == "wide"
+    assert bench.workload_family("llama3_8b_gqa_n8k_causal") == "wide"
+    assert bench.workload_family("long_n32k_causal") == "wide"
+    assert bench.workload_family("d256_h16_n8k_causal") == "ext"
+    assert bench.workload_family("outlier_b16h32_n2k") == "ext"        # N = 2048, 2^20 rows
     assert bench.workload_family("b4h16_n1k_d64") == "fwd"             # 2^16 rows, d = 64
     assert bench.workload_family("single_head_fp32") == "fwd"
     assert bench.workload_family("llama3_8b_gqa_decode_b8_n32k") == "decode"
     assert bench.workload_family("llama3_8b_n8k_causal_bwd") == "bwd"
     assert bench.workload_family("b1h16_n4k_bias") == "ext"
+    assert bench.workload_family("llama3_8b_n8k_causal_alibi") == "ext"
     assert bench.device_kernel("single_head_fp32") == "fa_fwd_f32_kernel"
     assert bench.device_kernel("b4h16_n1k_d64").startswith("fa_fwd_bf16_kernel")
-    assert bench.device_kernel("llama3_8b_n8k_causal").startswith("fa_fwd_ext_kernel")
+    assert bench.device_kernel("llama3_8b_n8k_causal").startswith("fa_fwd_wide_kernel")
+    assert bench.device_kernel("outlier_b16h32_n2k").startswith("fa_fwd_ext_kernel")
 
 
 def test_code_only_drops_comments_but_not_strings():
@@ -35,7 +41,9 @@ def test_code_only_drops_comments_but_not_strings():
 def test_digest_is_per_family_and_stable():
     d = {wl: bench.kernel_source_digest(wl) for wl in W.WORKLOADS}
     assert all(len(x) == 64 for x in d.values())
-    assert d["llama3_8b_n8k_causal"] == d["d256_h16_n8k_causal"]        # same family, same sources
+    assert d["llama3_8b_n8k_causal"] == d["long_n32k_causal"]           # same family, same sources
+    assert d["outlier_b16h32_n2k"] == d["d256_h16_n8k_causal"]
+    assert d["llama3_8b_n8k_causal"] != d["d256_h16_n8k_causal"]
     assert d["llama3_8b_n8k_causal"] != d["llama3_8b_n8k_causal_bwd"]
     assert d["llama3_8b_gqa_decode_b8_n32k"] != d["llama3_8b_n8k_causal_bwd"]
     assert bench.kernel_source_digest("llama3_8b_n8k_causal") == d["llama3_8b_n8k_causal"]
