@@ -33,6 +33,9 @@ def parse():
     ap.add_argument("--warmup", type=int, default=10)
     ap.add_argument("--workload", default="llama3_8b_n8k_causal")
     ap.add_argument("--no-cpu", action="store_true", help="skip the cpu_baseline leg")
+    ap.add_argument("--settle-ms", type=float, default=300.0,
+                    help="untimed launches for this long before the warm-up steps, so that the "
+                         "timed steps run at the GPU's loaded clock (0: none)")
     ap.add_argument("--cpu-heads", type=int, default=0,
                     help="max heads in the cpu_baseline sample (0 = all, capped at ~15 s)")
     ap.add_argument("--print-digest", action="store_true",
@@ -47,13 +50,24 @@ def host_info():
     """Cores available, CPU model and BLAS library of this host (for the cpu_baseline record)."""
     info = {"cores_available": len(os.sched_getaffinity(0))}
     try:
-        with open("/proc/cpuinfo") as f:
-            for line in f:
-                if line.startswith("model name"):
-                    info["cpu_model"] = line.split(":", 1)[1].strip()
-                    break
-    except OSError:
+        import subprocess
+        out = subprocess.run(["lscpu"], stdout=subprocess.PIPE, stderr=subprocess.DEVNULL,
+                             text=True, timeout=10).stdout
+        for line in out.splitlines():
+            if line.startswith("Model name:"):
+                info["cpu_model"] = line.split(":", 1)[1].strip()
+                break
+    except (OSError, subprocess.SubprocessError):
         pass
+    if "cpu_model" not in info:
+        try:
+            with open("/proc/cpuinfo") as f:
+                for line in f:
+                    if line.startswith("model name"):
+                        info["cpu_model"] = line.split(":", 1)[1].strip()
+                        break
+        except OSError:
+            pass
     try:
         from threadpoolctl import threadpool_info
         blas = [i for i in threadpool_info() if i.get("user_api") == "blas"]
@@ -92,35 +106,183 @@ def copy_calibration(nbytes, steps):
     print(json.dumps({"copy_bytes_per_launch": nbytes, "launches": steps}), flush=True)
 
 
+def gpu_sysfs_paths():
+    """sysfs files of the GPU: the shader clock table (pp_dpm_sclk, the current clock marked with
+    '*') and the socket power (hwmon power1_input, microwatts)."""
+    import glob
+    return (sorted(glob.glob("/sys/class/drm/card*/device/pp_dpm_sclk")),
+            sorted(glob.glob("/sys/class/drm/card*/device/hwmon/hwmon*/power1_input")))
+
+
+def parse_sclk(text):
+    """Current shader clock in MHz from a pp_dpm_sclk table (the line marked '*'), or None."""
+    import re
+    for line in text.splitlines():
+        if line.rstrip().endswith("*"):
+            m = re.search(r"(\d+)\s*[Mm]hz", line)
+            if m:
+                return int(m.group(1))
+    return None
+
+
+class ClockSampler:
+    """Samples the shader clock and the socket power from sysfs in a background thread, about
+    every millisecond (best effort: the record says null where the files are not readable)."""
+
+    def __init__(self):
+        import threading
+        self.clk_paths, self.pwr_paths = gpu_sysfs_paths()
+        self.samples = []
+        self._stop = threading.Event()
+        self._t = threading.Thread(target=self._run, daemon=True)
+
+    def _read(self, path):
+        try:
+            with open(path) as f:
+                return f.read()
+        except OSError:
+            return None
+
+    def _run(self):
+        while not self._stop.is_set():
+            now = time.perf_counter()
+            clk = [parse_sclk(t) for t in map(self._read, self.clk_paths) if t]
+            clk = [c for c in clk if c]
+            pwr = []
+            for t in map(self._read, self.pwr_paths):
+                try:
+                    pwr.append(int(t) / 1e6)
+                except (TypeError, ValueError):
+                    pass
+            if clk or pwr:
+                self.samples.append((now, max(clk) if clk else None, sum(pwr) if pwr else None))
+            time.sleep(0.001)
+
+    def __enter__(self):
+        if self.clk_paths or self.pwr_paths:
+            self._t.start()
+        return self
+
+    def __exit__(self, *exc):
+        self._stop.set()
+        if self.clk_paths or self.pwr_paths:
+            self._t.join()
+
+    def summary(self, t0, t1):
+        xs = [(c, p) for (t, c, p) in self.samples if t0 <= t <= t1]
+        if not xs:
+            return None
+        out = {"samples": len(xs)}
+        c = sorted(v for v, _ in xs if v is not None)
+        if c:
+            out.update(median_mhz=c[len(c) // 2], min_mhz=c[0], max_mhz=c[-1])
+        p = sorted(v for _, v in xs if v is not None)
+        if p:
+            out.update(median_w=round(p[len(p) // 2], 1))
+        return out
+
+
+def run_timed(step, stream, args):
+    """The timing protocol of every leg. Untimed launches for --settle-ms of wall time (the GPU
+    leaves its idle clock state: with only a few warm-up launches the first ~25 ms of load run at
+    a lower clock), then --warmup untimed steps, then exactly --steps steps timed with HIP events on
+    the launch stream, bracketed by device synchronisation. Returns (ms per step, wall seconds of
+    the timed region, record fields)."""
+    import torch
+    extra = {}
+    with ClockSampler() as clk:
+        t_settle = time.perf_counter()
+        n_settle = 0
+        if args.settle_ms > 0:
+            while (time.perf_counter() - t_settle) * 1e3 < args.settle_ms:
+                for _ in range(8):
+                    step()
+                n_settle += 8
+                torch.cuda.synchronize()
+        extra["settle"] = {"ms": round((time.perf_counter() - t_settle) * 1e3, 1),
+                           "launches": n_settle}
+        for _ in range(args.warmup):
+            step()
+        torch.cuda.synchronize()
+        e0 = torch.cuda.Event(enable_timing=True)
+        e1 = torch.cuda.Event(enable_timing=True)
+        t0 = time.perf_counter()
+        e0.record(stream)
+        for _ in range(args.steps):
+            step()
+        e1.record(stream)
+        torch.cuda.synchronize()
+        t1 = time.perf_counter()
+    extra["clock_during_timed_steps"] = clk.summary(t0, t1)
+    extra["clock_during_settle"] = clk.summary(t_settle, t_settle + extra["settle"]["ms"] / 1e3)
+    return e0.elapsed_time(e1) / args.steps, t1 - t0, extra
+
+
+def oracle_pool(tasks, budget_s=15.0, ram_bytes_per_task=0):
+    """Run the oracle tasks (callables) on a pool of one worker per available core, with BLAS held
+    to one thread per worker, in batches of one task per worker until the budget is spent (at
+    least one batch). Returns (tasks done, seconds, workers)."""
+    import concurrent.futures as cf
+    try:
+        from threadpoolctl import threadpool_limits
+    except Exception:  # pragma: no cover
+        threadpool_limits = None
+    workers = len(os.sched_getaffinity(0))
+    if ram_bytes_per_task:
+        try:
+            avail = os.sysconf("SC_AVPHYS_PAGES") * os.sysconf("SC_PAGE_SIZE")
+            workers = max(1, min(workers, int(avail * 0.5 // ram_bytes_per_task)))
+        except (OSError, ValueError):
+            pass
+    import contextlib
+    limit = threadpool_limits(limits=1, user_api="blas") if threadpool_limits else \
+        contextlib.nullcontext()
+    done, t0 = 0, time.perf_counter()
+    workers = max(1, min(workers, len(tasks)))
+    with limit, cf.ThreadPoolExecutor(max_workers=workers) as ex:
+        while done < len(tasks):
+            batch = tasks[done:done + workers]
+            list(ex.map(lambda f: f(), batch))
+            done += len(batch)
+            if time.perf_counter() - t0 >= budget_s:
+                break
+    return done, time.perf_counter() - t0, workers
+
+
 def cpu_baseline(q, k, v, scale, causal, w, n_heads, budget_s=15.0):
-    """Time the float64 oracle, as it stands, on whole heads (all their rows), in order, until
-    n_heads heads are done or budget_s seconds have passed (at least one head)."""
+    """Time the float64 oracle, as it stands, on a bounded sample of the workload: whole heads (or,
+    for workloads checked on sampled rows, those rows of every head), one head per worker."""
     import numpy as np
     from oracle import attention_head
-    try:
-        from threadpoolctl import threadpool_info
-        threads = max([i.get("num_threads", 1) for i in threadpool_info()
-                       if i.get("user_api") == "blas"] or [1])
-    except Exception:  # pragma: no cover
-        threads = 1
-    heads = [(b, h) for b in range(w["B"]) for h in range(w["H"])][:n_heads]
-    dt = 0.0
-    done = 0
-    group = w["H"] // w.get("H_kv", w["H"])  # query heads per K/V head
-    for b, h in heads:
-        qh = q[b, h].float().numpy().astype(np.float64)
-        kh, vh = (x[b, h // group].float().numpy().astype(np.float64) for x in (k, v))
-        t0 = time.perf_counter()
-        attention_head(qh, kh, vh, scale, causal)
-        dt += time.perf_counter() - t0
-        done += 1
-        if dt >= budget_s:
-            break
-    from exact_tiled_attention_05_amd.workloads import metric_flops
-    flops = metric_flops(1, done, w["N"], w["d"], causal)
-    return dict({"value": flops / dt / 1e12, "unit": "TFLOP/s", "cores": threads, "kind": "oracle",
-                 "sample": "%d of %d heads, every row (numpy float64, dense S and P), %.1f s"
-                           % (done, w["B"] * w["H"], dt)}, **host_info())
+    from exact_tiled_attention_05_amd import workloads as W
+    B, H, N, d = w["B"], w["H"], w["N"], w["d"]
+    group = H // w.get("H_kv", H)  # query heads per K/V head
+    rows = None
+    if w.get("sample_rows"):
+        rows = W.sampled_rows(N, w["sample_rows"], w["seed"])
+    heads = [(b, h) for b in range(B) for h in range(H)][:n_heads]
+
+    def task(b, h):
+        def run():
+            qh = q[b, h].float().numpy().astype(np.float64)
+            kh, vh = (x[b, h // group].float().numpy().astype(np.float64) for x in (k, v))
+            attention_head(qh, kh, vh, scale, causal, rows)
+        return run
+
+    R = N if rows is None else len(rows)
+    done, dt, workers = oracle_pool([task(b, h) for b, h in heads], budget_s,
+                                    ram_bytes_per_task=3 * R * N * 8)
+    if rows is None:
+        flops = W.metric_flops(1, done, N, d, causal)
+        what = "%d of %d heads, every row" % (done, B * H)
+    else:
+        per_row = [4 * ((i + 1) if causal else N) * d for i in rows]
+        flops = done * float(sum(per_row))
+        what = "%d of %d heads, the %d sampled rows of each (FLOPs 4*(i+1)*d per causal row i)" % (
+            done, B * H, len(rows))
+    return dict({"value": flops / dt / 1e12, "unit": "TFLOP/s", "cores": workers, "kind": "oracle",
+                 "sample": "%s; numpy float64 with dense S and P, one head per worker, BLAS at one "
+                           "thread per worker, %.1f s" % (what, dt)}, **host_info())
 
 
 def bench_decode(args, w):
@@ -153,19 +315,7 @@ def bench_decode(args, w):
         if rc != fa.FA_OK:
             raise fa.FAError(rc, "fa_fwd_splitkv")
 
-    for _ in range(args.warmup):
-        step()
-    torch.cuda.synchronize()
-    e0 = torch.cuda.Event(enable_timing=True)
-    e1 = torch.cuda.Event(enable_timing=True)
-    t0 = time.perf_counter()
-    e0.record(stream)
-    for _ in range(args.steps):
-        step()
-    e1.record(stream)
-    torch.cuda.synchronize()
-    wall = time.perf_counter() - t0
-    ms = e0.elapsed_time(e1) / args.steps
+    ms, wall, timing = run_timed(step, stream, args)
     kv_bytes = 2 * B * H_kv * Nkv * d * 2
     gbs = kv_bytes / (ms * 1e-3) / 1e9
     # algorithmic bytes of the step: K, V and Q read once, O and LSE written once (the split
@@ -188,31 +338,24 @@ def bench_decode(args, w):
         "wall_s_timed_region": round(wall, 4),
         "kernel_ms": per_launch_ms(step, stream),
     }
+    rec.update(timing)
     if not args.no_cpu:
-        try:
-            from threadpoolctl import threadpool_info
-            threads = max([i.get("num_threads", 1) for i in threadpool_info()
-                           if i.get("user_api") == "blas"] or [1])
-        except Exception:  # pragma: no cover
-            threads = 1
         group = H // H_kv
-        dt, done = 0.0, 0
-        for b in range(B):
-            for h in range(H):
+
+        def task(b, h):
+            def run():
                 qh = q[b, h].float().numpy().astype(np.float64)
                 kh, vh = (x[b, h // group].float().numpy().astype(np.float64) for x in (k, v))
-                t1 = time.perf_counter()
                 attention_head(qh, kh, vh, scale, causal, query_offset=Nkv - Nq)
-                dt += time.perf_counter() - t1
-                done += 1
-                if dt >= 15.0:
-                    break
-            if dt >= 15.0:
-                break
+            return run
+
+        done, dt, workers = oracle_pool([task(b, h) for b in range(B) for h in range(H)],
+                                        ram_bytes_per_task=3 * Nq * Nkv * 8)
         # each (b, h) reads its K/V head once: bytes of the heads done, at the oracle's rate
         rec["cpu_baseline"] = {"value": done * Nkv * d * 2 * 2 / dt / 1e9, "unit": "GB/s",
-                               "cores": threads, "kind": "oracle",
-                               "sample": "%d of %d (batch, head) pairs, numpy float64, %.1f s"
+                               "cores": workers, "kind": "oracle",
+                               "sample": "%d of %d (batch, head) pairs, numpy float64, one pair "
+                                         "per worker, BLAS at one thread per worker, %.1f s"
                                          % (done, B * H, dt)}
         rec["cpu_baseline"].update(host_info())
     print(json.dumps(rec), flush=True)
@@ -253,19 +396,7 @@ def bench_variant(args, w):
         if rc != fa.FA_OK:
             raise fa.FAError(rc, "fa_fwd_ext")
 
-    for _ in range(args.warmup):
-        step()
-    torch.cuda.synchronize()
-    e0 = torch.cuda.Event(enable_timing=True)
-    e1 = torch.cuda.Event(enable_timing=True)
-    t0 = time.perf_counter()
-    e0.record(stream)
-    for _ in range(args.steps):
-        step()
-    e1.record(stream)
-    torch.cuda.synchronize()
-    wall = time.perf_counter() - t0
-    ms = e0.elapsed_time(e1) / args.steps
+    ms, wall, timing = run_timed(step, stream, args)
     win = None if tuple(window) == (-1, -1) else tuple(window)
     flops = W.metric_flops_masked(B, H, N, d, causal, win)
     tflops = flops / (ms * 1e-3) / 1e12
@@ -285,33 +416,29 @@ def bench_variant(args, w):
         "wall_s_timed_region": round(wall, 4),
         "kernel_ms": per_launch_ms(step, stream),
     }
+    rec.update(timing)
     if not args.no_cpu:
-        try:
-            from threadpoolctl import threadpool_info
-            threads = max([i.get("num_threads", 1) for i in threadpool_info()
-                           if i.get("user_api") == "blas"] or [1])
-        except Exception:  # pragma: no cover
-            threads = 1
         group = H // H_kv
         sl = W.alibi_slopes(H).tolist() if w.get("alibi") else None
         bcpu = W.workload_bias(args.workload) if w.get("bias_seed") else None
-        dt, done = 0.0, 0
-        for h in range(H):
-            qh = q[0, h].float().numpy().astype(np.float64)
-            kh, vh = (x[0, h // group].float().numpy().astype(np.float64) for x in (k, v))
-            bm = bcpu[0, h].float().numpy().astype(np.float64) if bcpu is not None else None
-            t1 = time.perf_counter()
-            attention_head(qh, kh, vh, scale, causal, window=win,
-                           alibi_slope=None if sl is None else sl[h], bias=bm)
-            dt += time.perf_counter() - t1
-            done += 1
-            if dt >= 15.0:
-                break
+
+        def task(h):
+            def run():
+                qh = q[0, h].float().numpy().astype(np.float64)
+                kh, vh = (x[0, h // group].float().numpy().astype(np.float64) for x in (k, v))
+                bm = bcpu[0, h].float().numpy().astype(np.float64) if bcpu is not None else None
+                attention_head(qh, kh, vh, scale, causal, window=win,
+                               alibi_slope=None if sl is None else sl[h], bias=bm)
+            return run
+
+        done, dt, workers = oracle_pool([task(h) for h in range(H)],
+                                        ram_bytes_per_task=4 * N * N * 8)
         cflops = W.metric_flops_masked(1, done, N, d, causal, win)
-        rec["cpu_baseline"] = {"value": cflops / dt / 1e12, "unit": "TFLOP/s", "cores": threads,
+        rec["cpu_baseline"] = {"value": cflops / dt / 1e12, "unit": "TFLOP/s", "cores": workers,
                                "kind": "oracle",
                                "sample": "%d of %d heads of batch 0, every row (numpy float64, "
-                                         "dense S and P), %.1f s" % (done, B * H, dt)}
+                                         "dense S and P), one head per worker, BLAS at one thread "
+                                         "per worker, %.1f s" % (done, B * H, dt)}
         rec["cpu_baseline"].update(host_info())
     print(json.dumps(rec), flush=True)
 
@@ -349,19 +476,7 @@ def bench_backward(args, w):
         if rc != fa.FA_OK:
             raise fa.FAError(rc, "fa_bwd")
 
-    for _ in range(args.warmup):
-        step()
-    torch.cuda.synchronize()
-    e0 = torch.cuda.Event(enable_timing=True)
-    e1 = torch.cuda.Event(enable_timing=True)
-    t0 = time.perf_counter()
-    e0.record(stream)
-    for _ in range(args.steps):
-        step()
-    e1.record(stream)
-    torch.cuda.synchronize()
-    wall = time.perf_counter() - t0
-    ms = e0.elapsed_time(e1) / args.steps
+    ms, wall, timing = run_timed(step, stream, args)
     flops = W.metric_flops_bwd(B, H, N, d, causal)
     tflops = flops / (ms * 1e-3) / 1e12
     rec = {
@@ -380,29 +495,25 @@ def bench_backward(args, w):
         "wall_s_timed_region": round(wall, 4),
         "kernel_ms": per_launch_ms(step, stream),
     }
+    rec.update(timing)
     if not args.no_cpu:
-        try:
-            from threadpoolctl import threadpool_info
-            threads = max([i.get("num_threads", 1) for i in threadpool_info()
-                           if i.get("user_api") == "blas"] or [1])
-        except Exception:  # pragma: no cover
-            threads = 1
         group = H // H_kv
-        dt, done = 0.0, 0
-        for h in range(H):
-            qh, doh = (x[0, h].float().numpy().astype(np.float64) for x in (q, do))
-            kh, vh = (x[0, h // group].float().numpy().astype(np.float64) for x in (k, v))
-            t1 = time.perf_counter()
-            attention_backward_head(qh, kh, vh, doh, scale, causal)
-            dt += time.perf_counter() - t1
-            done += 1
-            if dt >= 15.0:
-                break
+
+        def task(h):
+            def run():
+                qh, doh = (x[0, h].float().numpy().astype(np.float64) for x in (q, do))
+                kh, vh = (x[0, h // group].float().numpy().astype(np.float64) for x in (k, v))
+                attention_backward_head(qh, kh, vh, doh, scale, causal)
+            return run
+
+        done, dt, workers = oracle_pool([task(h) for h in range(H)],
+                                        ram_bytes_per_task=6 * N * N * 8)
         cflops = W.metric_flops_bwd(1, done, N, d, causal)
-        rec["cpu_baseline"] = {"value": cflops / dt / 1e12, "unit": "TFLOP/s", "cores": threads,
+        rec["cpu_baseline"] = {"value": cflops / dt / 1e12, "unit": "TFLOP/s", "cores": workers,
                                "kind": "oracle",
                                "sample": "%d of %d heads of batch 0, every row (numpy float64, "
-                                         "dense S, P, dP, dS), %.1f s" % (done, B * H, dt)}
+                                         "dense S, P, dP, dS), one head per worker, BLAS at one "
+                                         "thread per worker, %.1f s" % (done, B * H, dt)}
         rec["cpu_baseline"].update(host_info())
     print(json.dumps(rec), flush=True)
 
@@ -541,22 +652,7 @@ def main():
         if rc != fa.FA_OK:
             raise fa.FAError(rc, fn.__name__)
 
-    for _ in range(args.warmup):
-        step()
-    torch.cuda.synchronize()
-
-    # Events are recorded on the stream the kernels are launched on.
-    e0 = torch.cuda.Event(enable_timing=True)
-    e1 = torch.cuda.Event(enable_timing=True)
-    torch.cuda.synchronize()
-    t0 = time.perf_counter()
-    e0.record(stream)
-    for _ in range(args.steps):
-        step()
-    e1.record(stream)
-    torch.cuda.synchronize()
-    wall = time.perf_counter() - t0
-    ms = e0.elapsed_time(e1) / args.steps
+    ms, wall, timing = run_timed(step, stream, args)
 
     flops = W.metric_flops(w["B"], w["H"], w["N"], w["d"], causal)
     tflops = flops / (ms * 1e-3) / 1e12
@@ -584,6 +680,7 @@ def main():
         "wall_s_timed_region": round(wall, 4),
         "kernel_ms": per_launch_ms(step, stream),
     }
+    rec.update(timing)
     if not args.no_cpu:
         n_heads = args.cpu_heads or w["B"] * w["H"]
         rec["cpu_baseline"] = cpu_baseline(q, k, v, scale, causal, w, n_heads)
