@@ -4,8 +4,9 @@ TEST INFRASTRUCTURE ONLY. The GPU is compared against ``oracle.attention``; this
 that the tests can show, on the CPU, that the blockwise recurrence the kernel implements reaches
 the dense max, sum and output for every way of cutting the keys into blocks.
 
-online_normalizer -- running (m, l) over a row that arrives in blocks, each block folded in with
-    its own block max and block sum and both partial sums moved to the new reference
+online_normalizer -- (m, l) of a row that arrives in blocks: each block is reduced to its own
+    (max, sum of exponentials) pair, and pairs are merged by moving both sums to the larger max;
+    the merge is associative, so the pairs are combined as a balanced tree
     ("Online Softmax & FlashAttention", §26.1, Eq 26.2; handbook §2.3).
 blockwise_row     -- the (m, l, a) merge for one query row: m' = max(m, max s), alpha = e^(m-m'),
     p = e^(s-m'), l' = alpha l + sum p, a' = alpha a + p^T V_b, o = a / l at the end
@@ -19,22 +20,39 @@ tiled_attention   -- the forward pass with query blocks outermost and key blocks
 import numpy as np
 
 
+def _block_summary(s):
+    """(max, sum of e^(s - max)) of one block; (-inf, 0) when no score in it is visible."""
+    s = np.asarray(s, dtype=np.float64)
+    if s.size == 0 or s.max() == -np.inf:
+        return -np.inf, 0.0
+    top = s.max()
+    return top, float(np.exp(s - top).sum())
+
+
+def _merge(x, y):
+    """Combine two (max, sum) summaries: both sums rescaled to the larger max (Eq 26.2)."""
+    (mx, lx), (my, ly) = x, y
+    top = max(mx, my)
+    if top == -np.inf:
+        return -np.inf, 0.0
+    return top, lx * np.exp(mx - top) + ly * np.exp(my - top)
+
+
 def online_normalizer(blocks):
-    """Return (m, l) of one score row given as a sequence of 1-D blocks (Eq 26.2 form)."""
-    m = -np.inf
-    ell = 0.0
-    for s in blocks:
-        s = np.asarray(s, dtype=np.float64)
-        if s.size == 0:
-            continue
-        m_b = s.max()
-        if m_b == -np.inf:
-            continue  # a block with no visible score adds nothing
-        ell_b = np.exp(s - m_b).sum()
-        m_new = max(m, m_b)
-        ell = np.exp(m - m_new) * ell + np.exp(m_b - m_new) * ell_b
-        m = m_new
-    return m, ell
+    """Return (m, l) of one score row given as a sequence of 1-D blocks.
+
+    Every block is summarised on its own, then neighbouring summaries are merged level by level
+    until one is left; the result equals the dense max and sum of e^(s - max) over the whole row.
+    """
+    level = [_block_summary(b) for b in blocks]
+    if not level:
+        return -np.inf, 0.0
+    while len(level) > 1:
+        nxt = [_merge(level[i], level[i + 1]) for i in range(0, len(level) - 1, 2)]
+        if len(level) % 2:
+            nxt.append(level[-1])
+        level = nxt
+    return level[0]
 
 
 def blockwise_row(s, v, bounds):

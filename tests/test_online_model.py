@@ -48,7 +48,8 @@ def _splits(n):
 
 @pytest.mark.parametrize("n", [1, 2, 5, 16, 23])
 def test_online_normalizer_equals_dense(n):
-    """Chapter 26 Eq 26.2 folded over any split gives the dense max and sum (north of 1e-12)."""
+    """Block summaries merged by Chapter 26 Eq 26.2 over any split give the dense max and sum
+    (to 1e-12 relative)."""
     s = RNG.standard_normal(n) * 5
     s_masked = s.copy()
     s_masked[n // 2 + 1:] = -np.inf  # a causal-style row: future keys are -inf
