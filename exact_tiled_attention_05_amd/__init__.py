@@ -34,6 +34,7 @@ Tensor convenience (PyTorch supplies device memory and the stream):
     backward(q, k, v, o, lse, dout, scale=None, causal=False, layout="bhnd", dq=None, dk=None,
              dv=None, workspace=None, stream=None) -> (dq, dk, dv)
 """
+import contextlib
 import ctypes
 import math
 import os
@@ -41,7 +42,7 @@ import os
 __all__ = ["fa_fwd", "fa_fwd_f32", "fa_fwd_gqa", "fa_fwd_gqa_f32", "fa_fwd_ext", "forward_ext",
            "fa_fwd_splitkv", "fa_fwd_splitkv_noalloc", "fa_bwd",
            "fa_bwd_workspace_bytes", "backward",
-           "fa_splitkv_workspace_bytes", "fa_strerror", "fa_version", "forward", "decode", "FAError", "library_path", "load_library", "FA_OK", "FA_ERR_INVALID_ARG",
+           "fa_splitkv_workspace_bytes", "fa_strerror", "fa_version", "forward", "decode", "FAError", "library_path", "race_check_library_path", "load_library", "using_library", "FA_OK", "FA_ERR_INVALID_ARG",
            "FA_ERR_UNSUPPORTED", "FA_ERR_ALIGNMENT", "FA_ERR_LAUNCH", "FA_ERR_TOO_LARGE",
            "FA_NOALLOC_SCRATCH_BYTES", "FA_LAYOUT_BHND", "FA_LAYOUT_BNHD"]
 
@@ -69,50 +70,77 @@ class FAError(RuntimeError):
         super().__init__("%s failed: %s (code %d)" % (where, fa_strerror(code), code))
 
 
-def load_library():
-    """Load libfa.so from the package directory (built by ``exact_tiled_attention_05_amd.build``)."""
+def race_check_library_path():
+    return os.path.join(_HERE, "libfa_race.so")
+
+
+def load_library(path=None):
+    """Load libfa.so from the package directory (built by ``exact_tiled_attention_05_amd.build``).
+
+    With ``path`` (e.g. ``race_check_library_path()``) that build of the same C-ABI is loaded and
+    returned instead; the module's own entry points keep using libfa.so.
+    """
     global _LIB
+    if path is not None:
+        return _open(path)
     if _LIB is None:
-        path = library_path()
-        if not os.path.exists(path):
-            raise RuntimeError("libfa.so is not built (expected at %s); run "
-                               "`python -m exact_tiled_attention_05_amd.build`" % path)
-        lib = ctypes.CDLL(path)
-        fwd_args = [ctypes.c_void_p] * 5 + [ctypes.c_int] * 4 + [ctypes.c_float, ctypes.c_int,
-                                                                   ctypes.c_void_p]
-        gqa_args = [ctypes.c_void_p] * 5 + [ctypes.c_int] * 5 + [ctypes.c_float, ctypes.c_int,
-                                                                   ctypes.c_int, ctypes.c_void_p]
-        for name, argt in (("fa_fwd", fwd_args), ("fa_fwd_f32", fwd_args),
-                           ("fa_fwd_gqa", gqa_args), ("fa_fwd_gqa_f32", gqa_args)):
-            fn = getattr(lib, name)
-            fn.argtypes = argt
-            fn.restype = ctypes.c_int
-        lib.fa_fwd_ext.argtypes = ([ctypes.c_void_p] * 5 + [ctypes.c_int] * 5 + [ctypes.c_float] +
-                                   [ctypes.c_int] * 4 + [ctypes.c_void_p] * 2 +
-                                   [ctypes.c_longlong] * 3 + [ctypes.c_void_p])
-        lib.fa_fwd_ext.restype = ctypes.c_int
-        lib.fa_splitkv_workspace_bytes.argtypes = [ctypes.c_int] * 8
-        lib.fa_splitkv_workspace_bytes.restype = ctypes.c_size_t
-        lib.fa_fwd_splitkv.argtypes = ([ctypes.c_void_p] * 5 + [ctypes.c_int] * 6 +
-                                       [ctypes.c_float] + [ctypes.c_int] * 3 +
-                                       [ctypes.c_void_p, ctypes.c_size_t, ctypes.c_void_p])
-        lib.fa_fwd_splitkv.restype = ctypes.c_int
-        lib.fa_fwd_splitkv_noalloc.argtypes = ([ctypes.c_void_p] * 5 + [ctypes.c_int] * 6 +
-                                               [ctypes.c_float] + [ctypes.c_int] * 3 +
-                                               [ctypes.c_void_p])
-        lib.fa_fwd_splitkv_noalloc.restype = ctypes.c_int
-        lib.fa_bwd_workspace_bytes.argtypes = [ctypes.c_int] * 5
-        lib.fa_bwd_workspace_bytes.restype = ctypes.c_size_t
-        lib.fa_bwd.argtypes = ([ctypes.c_void_p] * 9 + [ctypes.c_int] * 5 + [ctypes.c_float] +
-                               [ctypes.c_int] * 2 + [ctypes.c_void_p, ctypes.c_size_t,
-                                                     ctypes.c_void_p])
-        lib.fa_bwd.restype = ctypes.c_int
-        lib.fa_strerror.argtypes = [ctypes.c_int]
-        lib.fa_strerror.restype = ctypes.c_char_p
-        lib.fa_version.argtypes = []
-        lib.fa_version.restype = ctypes.c_int
-        _LIB = lib
+        _LIB = _open(library_path())
     return _LIB
+
+
+@contextlib.contextmanager
+def using_library(lib):
+    """Inside the block, this module's entry points call ``lib`` (a library returned by
+    ``load_library(path)``) instead of libfa.so. Not thread-safe: it swaps a module global."""
+    global _LIB
+    prev = load_library()
+    _LIB = lib
+    try:
+        yield lib
+    finally:
+        _LIB = prev
+
+
+def _open(path):
+    if not os.path.exists(path):
+        raise RuntimeError("%s is not built (expected at %s); run "
+                           "`python -m exact_tiled_attention_05_amd.build --all`"
+                           % (os.path.basename(path), path))
+    lib = ctypes.CDLL(path)
+    fwd_args = [ctypes.c_void_p] * 5 + [ctypes.c_int] * 4 + [ctypes.c_float, ctypes.c_int,
+                                                               ctypes.c_void_p]
+    gqa_args = [ctypes.c_void_p] * 5 + [ctypes.c_int] * 5 + [ctypes.c_float, ctypes.c_int,
+                                                               ctypes.c_int, ctypes.c_void_p]
+    for name, argt in (("fa_fwd", fwd_args), ("fa_fwd_f32", fwd_args),
+                       ("fa_fwd_gqa", gqa_args), ("fa_fwd_gqa_f32", gqa_args)):
+        fn = getattr(lib, name)
+        fn.argtypes = argt
+        fn.restype = ctypes.c_int
+    lib.fa_fwd_ext.argtypes = ([ctypes.c_void_p] * 5 + [ctypes.c_int] * 5 + [ctypes.c_float] +
+                               [ctypes.c_int] * 4 + [ctypes.c_void_p] * 2 +
+                               [ctypes.c_longlong] * 3 + [ctypes.c_void_p])
+    lib.fa_fwd_ext.restype = ctypes.c_int
+    lib.fa_splitkv_workspace_bytes.argtypes = [ctypes.c_int] * 8
+    lib.fa_splitkv_workspace_bytes.restype = ctypes.c_size_t
+    lib.fa_fwd_splitkv.argtypes = ([ctypes.c_void_p] * 5 + [ctypes.c_int] * 6 +
+                                   [ctypes.c_float] + [ctypes.c_int] * 3 +
+                                   [ctypes.c_void_p, ctypes.c_size_t, ctypes.c_void_p])
+    lib.fa_fwd_splitkv.restype = ctypes.c_int
+    lib.fa_fwd_splitkv_noalloc.argtypes = ([ctypes.c_void_p] * 5 + [ctypes.c_int] * 6 +
+                                           [ctypes.c_float] + [ctypes.c_int] * 3 +
+                                           [ctypes.c_void_p])
+    lib.fa_fwd_splitkv_noalloc.restype = ctypes.c_int
+    lib.fa_bwd_workspace_bytes.argtypes = [ctypes.c_int] * 5
+    lib.fa_bwd_workspace_bytes.restype = ctypes.c_size_t
+    lib.fa_bwd.argtypes = ([ctypes.c_void_p] * 9 + [ctypes.c_int] * 5 + [ctypes.c_float] +
+                           [ctypes.c_int] * 2 + [ctypes.c_void_p, ctypes.c_size_t,
+                                                 ctypes.c_void_p])
+    lib.fa_bwd.restype = ctypes.c_int
+    lib.fa_strerror.argtypes = [ctypes.c_int]
+    lib.fa_strerror.restype = ctypes.c_char_p
+    lib.fa_version.argtypes = []
+    lib.fa_version.restype = ctypes.c_int
+    return lib
 
 
 def fa_fwd(q, k, v, o, lse, B, H, N, d, scale, causal, stream=None):

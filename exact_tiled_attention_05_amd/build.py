@@ -1,6 +1,7 @@
 """Build libfa.so (the C-ABI attention library) in-tree with hipcc for gfx950.
 
-Usage: ``python -m exact_tiled_attention_05_amd.build`` or ``build()`` from Python. The library
+Usage: ``python -m exact_tiled_attention_05_amd.build [--all]`` or ``build()`` / ``build_all()``
+from Python (``--all`` / ``build_all`` also build the race-check library). The library
 lands next to this file, where the Python binding loads it from. Each translation unit is compiled
 to an object with its own flags, then the objects are linked into one shared library.
 """
@@ -13,6 +14,10 @@ ROOT = os.path.dirname(PKG_DIR)
 CSRC = os.path.join(PKG_DIR, "csrc")
 INCLUDE = os.path.join(ROOT, "include")
 LIB_PATH = os.path.join(PKG_DIR, "libfa.so")
+# The same sources built with FA_RACE_CHECK=1: every LDS tile load completes before any wave goes
+# on and LDS starts filled with NaN (see fa_device.h); the tests compare it with libfa.so bit for
+# bit.
+RACE_CHECK_LIB_PATH = os.path.join(PKG_DIR, "libfa_race.so")
 
 # Packed fp32 VALU instructions are disabled for all device code. NaNs are never produced by the
 # kernels for finite inputs (hidden keys are -inf, never 0*inf), so max needs no NaN handling.
@@ -70,5 +75,15 @@ def build(verbose=False, extra_flags=(), out=LIB_PATH):
     return out
 
 
+def build_all(verbose=False):
+    """Build libfa.so and its race-check twin libfa_race.so."""
+    build(verbose=verbose)
+    build(verbose=verbose, extra_flags=["-DFA_RACE_CHECK=1"], out=RACE_CHECK_LIB_PATH)
+
+
 if __name__ == "__main__":
-    print(build(verbose="-v" in sys.argv))
+    if "--all" in sys.argv:
+        build_all(verbose="-v" in sys.argv)
+        print(LIB_PATH, RACE_CHECK_LIB_PATH)
+    else:
+        print(build(verbose="-v" in sys.argv))

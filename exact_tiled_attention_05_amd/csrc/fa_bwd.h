@@ -80,6 +80,9 @@ __global__ __launch_bounds__(kBwdQWaves * 64) __attribute__((amdgpu_waves_per_eu
   const int tid = threadIdx.x, lane = tid & 63;
   const int wave = __builtin_amdgcn_readfirstlane(tid >> 6);  // uniform: keeps wave tests scalar
   const int c = lane & 31, h = lane >> 5;
+  race_check_poison<sizeof(sK2)>(sK2, tid, kBwdQWaves * 64);
+  race_check_poison<sizeof(sV2)>(sV2, tid, kBwdQWaves * 64);
+  race_check_barrier();
   int bh, qblk;
   map_block<CAUSAL>(blockIdx.x, gridDim.x, a.BH, a.n_qblk, bh, qblk);
   const int b = bh / a.H, hq = bh - b * a.H, hk = hq / a.group;
@@ -140,6 +143,7 @@ __global__ __launch_bounds__(kBwdQWaves * 64) __attribute__((amdgpu_waves_per_eu
       dma_tile<D, kBwdTile, W>(sK2[stg ^ 1], kh, rs, (j + 1) * kBwdTile, N, wave, lane);
       dma_tile<D, kBwdTile, W>(sV2[stg ^ 1], vh, rs, (j + 1) * kBwdTile, N, wave, lane);
     }
+    race_check_drain();
     const char* sK = sK2[stg];
     const char* sV = sV2[stg];
 #pragma unroll
@@ -232,6 +236,12 @@ __global__ __launch_bounds__(kBwdKvWaves * 64) __attribute__((amdgpu_waves_per_e
   const int tid = threadIdx.x, lane = tid & 63;
   const int wave = __builtin_amdgcn_readfirstlane(tid >> 6);  // uniform: keeps wave tests scalar
   const int c = lane & 31, h = lane >> 5;
+  race_check_poison<sizeof(sQ2)>(sQ2, tid, kBwdKvWaves * 64);
+  race_check_poison<sizeof(sO2)>(sO2, tid, kBwdKvWaves * 64);
+  race_check_poison<sizeof(sL2)>(sL2, tid, kBwdKvWaves * 64);
+  race_check_poison<sizeof(sD2)>(sD2, tid, kBwdKvWaves * 64);
+  race_check_poison<sizeof(sVb)>(sVb, tid, kBwdKvWaves * 64);
+  race_check_barrier();
   int vh, x;  // vh: (batch * K/V head, query-head split)
   map_block<CAUSAL>(blockIdx.x, gridDim.x, a.BHkv * a.hsplit, a.n_kblk, vh, x);
   const int kblk = CAUSAL ? a.n_kblk - 1 - x : x;  // causal: the first key blocks, which see the
@@ -302,6 +312,7 @@ __global__ __launch_bounds__(kBwdKvWaves * 64) __attribute__((amdgpu_waves_per_e
     constexpr int stg = decltype(stage_c)::value;
     const int t = t0 + s % (n_qt - t0);
     if (s + 1 < n_steps) issue_step(s + 1);
+    race_check_drain();
     const char* sQ = sQ2[stg];
     const char* sO = sO2[stg];
     const float* sL = sL2[stg];
@@ -366,6 +377,7 @@ __global__ __launch_bounds__(kBwdKvWaves * 64) __attribute__((amdgpu_waves_per_e
     }
     if (s + 1 < n_steps) {
       wait_dma();
+      race_check_barrier();
       publish_step(s + 1);
       __syncthreads();
     }

@@ -13,6 +13,33 @@ typedef float f32x16 __attribute__((ext_vector_type(16)));
 
 #define FA_LDS __attribute__((address_space(3)))
 
+// Race-check build (compiled with -DFA_RACE_CHECK=1). The kernels overlap the loads of the next
+// K/V tiles into LDS with the products on the current ones; a missing wait or barrier there would
+// let a wave read a tile before it has landed, or let a load overwrite a tile a wave still reads.
+// In this build every tile load completes, for every wave of the work-group, before any wave goes
+// on (a full wait and a barrier right after the loads are issued, a barrier before a staged store),
+// and LDS starts filled with all-ones bytes (NaN as bf16 and as fp32). The arithmetic and its order
+// are unchanged, so a race-free fast build gives bit-identical outputs; a race shows as a
+// difference, and a read of LDS that no load wrote shows as NaN.
+#ifndef FA_RACE_CHECK
+#define FA_RACE_CHECK 0
+#endif
+
+// Every thread of the work-group fills its share of an LDS array; followed by a barrier.
+template <int BYTES>
+__device__ __forceinline__ void race_check_poison(void* lds, int tid, int nthreads) {
+  if constexpr (FA_RACE_CHECK != 0) {
+    static_assert(BYTES % 16 == 0, "LDS arrays are filled 16 bytes at a time");
+    typedef unsigned u32x4p __attribute__((ext_vector_type(4)));
+    for (int i = 16 * tid; i < BYTES; i += 16 * nthreads)
+      *(FA_LDS u32x4p*)((FA_LDS char*)lds + i) = u32x4p{~0u, ~0u, ~0u, ~0u};
+  }
+}
+// A barrier in the race-check build only (called where the whole work-group passes).
+__device__ __forceinline__ void race_check_barrier() {
+  if constexpr (FA_RACE_CHECK != 0) __syncthreads();
+}
+
 constexpr float kLog2e = 1.4426950408889634f;
 constexpr float kLn2 = 0.6931471805599453f;
 

@@ -283,6 +283,15 @@ __global__ __launch_bounds__(kNumWaves * 64) void fa_fwd_bf16_kernel(Bf16Args a)
   const int wave = __builtin_amdgcn_readfirstlane(threadIdx.x >> 6);
   const bool group_a = wave < kNumWaves / 2;  // waves w and w + 4 share a SIMD
   const int N = a.N;
+  {
+    race_check_poison<Layout<D>::K_BYTES>(sK0, threadIdx.x, kNumWaves * 64);
+    race_check_poison<Layout<D>::K_BYTES>(sK1, threadIdx.x, kNumWaves * 64);
+    race_check_poison<Layout<D>::K_BYTES>(sK2, threadIdx.x, kNumWaves * 64);
+    race_check_poison<Layout<D>::V_BYTES>(sV0, threadIdx.x, kNumWaves * 64);
+    race_check_poison<Layout<D>::V_BYTES>(sV1, threadIdx.x, kNumWaves * 64);
+    race_check_poison<Layout<D>::V_BYTES>(sV2, threadIdx.x, kNumWaves * 64);
+    race_check_barrier();
+  }
 
   int bh, qblk;
   map_block<CAUSAL>(blockIdx.x, gridDim.x, a.BH, a.n_qblk, bh, qblk);
@@ -352,6 +361,7 @@ __global__ __launch_bounds__(kNumWaves * 64) void fa_fwd_bf16_kernel(Bf16Args a)
 
   // Crossing j: staged tile j+1 into its stage, barrier, loads of tile j+2.
   auto crossing = [&](char* __restrict__ Kn, char* __restrict__ Vn, int j) {
+    race_check_barrier();
     store_tile<D>(Kn, Vn, wave, lane, stage);
     __syncthreads();
     if (j + 2 < n_kt) load_tile<D>(src, (j + 2) * kBlockK, N, wave, stage);

@@ -106,6 +106,10 @@ __global__ __launch_bounds__(kExtWaves * 64) __attribute__((amdgpu_waves_per_eu(
   const int tid = threadIdx.x, lane = tid & 63;
   const int wave = __builtin_amdgcn_readfirstlane(tid >> 6);
   const int c = lane & 31, h = lane >> 5;
+  race_check_poison<sizeof(sK2)>(sK2, tid, kExtWaves * 64);
+  race_check_poison<sizeof(sV2)>(sV2, tid, kExtWaves * 64);
+  race_check_poison<sizeof(sB2)>(sB2, tid, kExtWaves * 64);
+  race_check_barrier();
   int bh, qblk;
   map_block<CAUSAL>(blockIdx.x, gridDim.x, a.BH, a.n_qblk, bh, qblk);
   const int b = bh / a.H, hq = bh - b * a.H, hk = hq / a.group;
@@ -218,6 +222,7 @@ __global__ __launch_bounds__(kExtWaves * 64) __attribute__((amdgpu_waves_per_eu(
         bias_issued = true;
       }
     }
+    race_check_drain();
     const char* sK = sK2[st];
     const char* sV = sV2[st];
     const char* sB = sB2[bst];

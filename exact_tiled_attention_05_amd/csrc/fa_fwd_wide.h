@@ -276,6 +276,9 @@ __global__ __launch_bounds__(kWideWaves * 64) __attribute__((amdgpu_waves_per_eu
   const int tid = threadIdx.x, lane = tid & 63;
   const int wave = __builtin_amdgcn_readfirstlane(tid >> 6);
   const int c = lane & 31, h = lane >> 5;
+  race_check_poison<NS * TILE>(sK, tid, kWideWaves * 64);
+  race_check_poison<NS * TILE>(sV, tid, kWideWaves * 64);
+  race_check_barrier();
   int bh, qblk;
   map_block<CAUSAL>(blockIdx.x, gridDim.x, a.BH, a.n_qblk, bh, qblk);
   const int b = bh / a.H, hq = bh - b * a.H, hk = hq / a.group;
@@ -353,6 +356,7 @@ __global__ __launch_bounds__(kWideWaves * 64) __attribute__((amdgpu_waves_per_eu
   } else {
     wait_dma();
   }
+  race_check_drain();
   __syncthreads();
   load_k(sK[0], 0);
   {
@@ -397,6 +401,7 @@ __global__ __launch_bounds__(kWideWaves * 64) __attribute__((amdgpu_waves_per_eu
         }
       }
     });
+    if constexpr (LAST) race_check_drain();
     if (__builtin_expect(k0 + 31 > edgeB, 0)) wide_mask(B, k0, lastB, h);
     wide_check(B);
     // P3: S_A(j+1) = K(j+1) Q_A^T; probabilities of B, step j

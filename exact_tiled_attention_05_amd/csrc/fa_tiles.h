@@ -106,6 +106,13 @@ __device__ __forceinline__ void wait_vmcnt() {
   __builtin_amdgcn_s_waitcnt((N & 15) | ((N >> 4) << 14) | (7 << 4) | (15 << 8));
 }
 __device__ __forceinline__ void wait_dma() { wait_vmcnt<0>(); }
+// Race-check build: the loads just issued land before any wave of the work-group goes on.
+__device__ __forceinline__ void race_check_drain() {
+  if constexpr (FA_RACE_CHECK != 0) {
+    wait_dma();
+    __syncthreads();
+  }
+}
 // Wait for all but the N most recently issued loads (loads complete in issue order for vmcnt).
 template <int N>
 __device__ __forceinline__ void wait_dma_but() { wait_vmcnt<N>(); }

@@ -32,10 +32,14 @@ def test_header_declares_the_expected_entry_points():
                            "fa_version"]
 
 
-def test_library_exports_every_declared_symbol():
-    lib = ctypes.CDLL(fa.library_path())
+@pytest.mark.parametrize("path", [fa.library_path(), fa.race_check_library_path()],
+                         ids=["libfa", "libfa_race"])
+def test_library_exports_every_declared_symbol(path):
+    """Both builds (the fast library and its race-check twin) export the whole C-ABI."""
+    lib = ctypes.CDLL(path)
     for name in _declared():
         assert hasattr(lib, name), name
+    assert fa.load_library(path).fa_version() == fa.load_library().fa_version()
 
 
 def test_python_codes_match_header():
