@@ -263,17 +263,18 @@ int run_f32(const float* q, const float* k, const float* v, float* o, float* lse
 
 // ---- split-KV decoding ------------------------------------------------------------------------
 
-// Splits: about 768 (batch, K/V head, split) waves in all, three per CU, but at least 128 keys per
-// split; a caller's count is honoured up to one split per 32 keys. Fewer, longer K/V streams read
+// Splits: about 768 (batch, K/V head, split, row tile) waves in all, three per CU, but at least
+// 128 keys per split; a caller's count is honoured up to one split per 32 keys. Fewer, longer K/V streams read
 // faster than a full 8 waves per CU: on the Llama-3-8B decoding batch (64 K/V heads, 32768 keys)
 // 12 splits take 163 us where 32 take 180 us, and 512-768 waves were best on every shape measured.
 struct SplitPlan {
   int n_splits, keys_per_split;
 };
-SplitPlan plan_splits(int B, int H_kv, int N_kv, int n_splits) {
+SplitPlan plan_splits(int B, int H_kv, int N_kv, int R, int n_splits) {
   int n = n_splits;
   if (n <= 0) {
-    const int want = (768 + B * H_kv - 1) / (B * H_kv);
+    const int tiles = (R + fa::kDecodeRows - 1) / fa::kDecodeRows;
+    const int want = (768 + B * H_kv * tiles - 1) / (B * H_kv * tiles);
     n = std::max(1, std::min(want, (N_kv + 127) / 128));
   }
   n = std::min(n, (N_kv + 31) / 32);
@@ -297,15 +298,18 @@ int check_decode_shape(int B, int H, int H_kv, int N_q, int N_kv, int d, int cau
   if (causal && N_q > N_kv) return FA_ERR_INVALID_ARG;
   if (n_splits < 0) return FA_ERR_INVALID_ARG;
   if (d != 64 && d != 128) return FA_ERR_UNSUPPORTED;
-  if ((int64_t)(H / H_kv) * N_q > fa::kDecodeRows) return FA_ERR_UNSUPPORTED;
+  if ((int64_t)(H / H_kv) * N_q > fa::kDecodeMaxRows) return FA_ERR_UNSUPPORTED;
   return FA_OK;
 }
 
 template <int D>
 hipError_t launch_decode(fa::DecodeArgs a, hipStream_t s) {
   void* args[] = {&a};
+  // one row tile: a wave per split; several: the splits padded to a multiple of 8 (the kernel's
+  // XCD-grouped numbering), T waves each
+  const int gx = a.row_tiles == 1 ? a.n_splits : (a.n_splits + 7) / 8 * 8 * a.row_tiles;
   hipError_t e = hipLaunchKernel(reinterpret_cast<const void*>(&fa::fa_decode_partial_kernel<D>),
-                                 dim3(a.n_splits, a.B_Hkv()), dim3(64), args, 0, s);
+                                 dim3(gx, a.B_Hkv()), dim3(64), args, 0, s);
   if (e != hipSuccess) return e;
   return hipLaunchKernel(reinterpret_cast<const void*>(&fa::fa_decode_combine_kernel<D>),
                          dim3(a.R, a.B_Hkv()), dim3(fa::kCombineThreads), args, 0, s);
@@ -353,8 +357,8 @@ int run_splitkv(const void* q, const void* k, const void* v, void* o, float* lse
   if (!q || !k || !v || !o || !lse || (!static_scratch && !workspace)) return FA_ERR_INVALID_ARG;
   int rc = check_decode_shape(B, H, H_kv, N_q, N_kv, d, causal, n_splits);
   if (rc != FA_OK) return rc;
-  const SplitPlan sp = plan_splits(B, H_kv, N_kv, n_splits);
   const int R = (H / H_kv) * N_q;
+  const SplitPlan sp = plan_splits(B, H_kv, N_kv, R, n_splits);
   const size_t need = ws_bytes(B, H_kv, R, d, sp.n_splits);
   if (static_scratch && need > FA_NOALLOC_SCRATCH_BYTES) return FA_ERR_TOO_LARGE;
   if (layout != FA_LAYOUT_BHND && layout != FA_LAYOUT_BNHD) return FA_ERR_INVALID_ARG;
@@ -398,6 +402,7 @@ int run_splitkv(const void* q, const void* k, const void* v, void* o, float* lse
   a.group = H / H_kv;
   a.B = B;
   a.R = R;
+  a.row_tiles = (R + fa::kDecodeRows - 1) / fa::kDecodeRows;
   a.n_splits = sp.n_splits;
   a.keys_per_split = sp.keys_per_split;
   a.causal = causal;
@@ -537,8 +542,9 @@ int fa_bwd(const void* q, const void* k, const void* v, const void* o, const voi
 size_t fa_splitkv_workspace_bytes(int B, int H, int H_kv, int N_q, int N_kv, int d, int causal,
                                   int n_splits) {
   if (check_decode_shape(B, H, H_kv, N_q, N_kv, d, causal, n_splits) != FA_OK) return 0;
-  const SplitPlan sp = plan_splits(B, H_kv, N_kv, n_splits);
-  return ws_bytes(B, H_kv, (H / H_kv) * N_q, d, sp.n_splits);
+  const int R = (H / H_kv) * N_q;
+  const SplitPlan sp = plan_splits(B, H_kv, N_kv, R, n_splits);
+  return ws_bytes(B, H_kv, R, d, sp.n_splits);
 }
 
 int fa_fwd_splitkv(const void* q, const void* k, const void* v, void* o, float* lse, int B, int H,
@@ -586,7 +592,7 @@ const char* fa_strerror(int code) {
              "workspace that is too small)";
     case FA_ERR_UNSUPPORTED:
       return "unsupported shape (head dimension not 64 or 128 -- or 256 on the bf16 forward "
-             "entry points --, or more than 32 query rows per K/V head in split-KV decoding)";
+             "entry points --, or more than 512 query rows per K/V head in split-KV decoding)";
     case FA_ERR_ALIGNMENT:
       return "pointer not 16-byte aligned";
     case FA_ERR_LAUNCH:

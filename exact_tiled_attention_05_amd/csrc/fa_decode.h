@@ -9,10 +9,12 @@
 //     LSE = M + ln sum_s e^{LSE_s - M},   O = sum_s e^{LSE_s - LSE} O_s      (M = max_s LSE_s).
 //
 // Two kernels.
-//   fa_decode_partial_kernel: one wave per (batch, K/V head, key split). The G = H / H_kv query
-//     heads of that K/V head and their N_q query rows are stacked into one 32-row MFMA tile
-//     (row r = g * N_q + i; requires G * N_q <= 32), so every K/V byte is read once for all of
-//     them. Per 32-key step: K and V come from memory in whole rows (non-temporal buffer loads)
+//   fa_decode_partial_kernel: one wave per (batch, K/V head, key split, 32-row tile). The G =
+//     H / H_kv query heads of that K/V head and their N_q query rows are stacked into R = G N_q
+//     rows (row r = g * N_q + i), cut into 32-row MFMA tiles; with R <= 32 one wave reads every
+//     K/V byte of its split once for all of them. With more rows the waves of one split's tiles
+//     are numbered so that they run on the same XCD one after another, and all but the first find
+//     the split's K/V in that XCD's L2. Per 32-key step: K and V come from memory in whole rows (non-temporal buffer loads)
 //     into wave-private LDS tiles, laid out as in the prefill kernel, and are read back as MFMA
 //     operands (V with the transposing read); S^T = K Q^T and O^T += V^T P^T on
 //     v_mfma_f32_32x32x16_bf16, the online softmax with an exact running maximum. The next step's
@@ -33,7 +35,8 @@
 
 namespace fa {
 
-constexpr int kDecodeRows = 32;  // stacked query rows per wave (one MFMA tile)
+constexpr int kDecodeRows = 32;       // stacked query rows per wave (one MFMA tile)
+constexpr int kDecodeMaxRows = 512;   // stacked query rows per K/V head, 16 tiles
 // Cache-policy operand of the decode kernel's K/V loads: bit 1 is the non-temporal hint (each K/V
 // byte is read once per call, so its lines go first when L2 needs room).
 constexpr int kStreamLoad = 2;
@@ -48,7 +51,8 @@ struct DecodeArgs {
   float* ws_lse;  // [B * H_kv][n_splits][R] fp32 partial logsumexps
   int Nq, Nkv;
   int B, H, Hkv, group;  // batch, query heads, K/V heads, query heads per K/V head
-  int R;                 // stacked rows = group * Nq (<= 32)
+  int R;                 // stacked rows = group * Nq (<= kDecodeMaxRows)
+  int row_tiles;         // ceil(R / 32)
   int n_splits, keys_per_split;
   int causal, causal_off;  // causal_off = Nkv - Nq
   float scale_log2;
@@ -74,7 +78,18 @@ __global__ __launch_bounds__(64) __attribute__((amdgpu_waves_per_eu(2))) void fa
   __shared__ __attribute__((aligned(1024))) char sV[32 * VROW];
 
   const int lane = threadIdx.x;
-  const int s = blockIdx.x, bk = blockIdx.y;
+  const int bk = blockIdx.y;
+  // (split, row tile) of this wave. One tile: x is the split. Several: x = 8 (T (s / 8) + t) +
+  // s mod 8 for split s and tile t of T, so that (with the grid's x extent a multiple of 8 and
+  // workgroups dealt to the 8 XCDs in turn) every tile of a split runs on XCD s mod 8, the T of
+  // them consecutively there. x past the last split exits (the whole one-wave workgroup).
+  int s = blockIdx.x, rt = 0;
+  if (a.row_tiles > 1) {
+    const int T = a.row_tiles, u = blockIdx.x >> 3;
+    rt = u % T;
+    s = (u / T) * 8 + (blockIdx.x & 7);
+    if (s >= a.n_splits) return;
+  }
   const int b = bk / a.Hkv, hk = bk - b * a.Hkv;
   const int key_begin = s * a.keys_per_split;
   const int key_end = min(a.Nkv, key_begin + a.keys_per_split);
@@ -89,14 +104,15 @@ __global__ __launch_bounds__(64) __attribute__((amdgpu_waves_per_eu(2))) void fa
     L.kbase = L.c * KROW + 16 * L.h;
     L.vbase = (4 * L.h + (Lg >> 2)) * VROW + 2 * (16 * ((lane >> 4) & 1) + 4 * (Lg & 3));
   }
-  const bool row_ok = L.c < a.R;
+  const int row = 32 * rt + L.c;  // this lane's stacked row
+  const bool row_ok = row < a.R;
   // query index of this lane's stacked row (for the causal limit)
-  const int qi = row_ok ? L.c % a.Nq : 0;
+  const int qi = row_ok ? row % a.Nq : 0;
   const int key_limit = a.causal ? min(key_end - 1, qi + a.causal_off) : key_end - 1;
 
   bf16x8 qf[DK];
   {
-    const bf16* qrow = a.q + (row_ok ? decode_q_offset(a, b, hk, L.c) : 0);
+    const bf16* qrow = a.q + (row_ok ? decode_q_offset(a, b, hk, row) : 0);
 #pragma unroll
     for (int dk = 0; dk < DK; dk++)
       qf[dk] = row_ok ? *reinterpret_cast<const bf16x8*>(qrow + dk * 16 + L.h * 8) : bf16x8{};
@@ -191,7 +207,7 @@ __global__ __launch_bounds__(64) __attribute__((amdgpu_waves_per_eu(2))) void fa
   // (0, -inf) if the row saw no key here.
   const float lt = half_swap_sum(l);
   if (row_ok) {
-    const long long slot = ((long long)bk * a.n_splits + s) * a.R + L.c;
+    const long long slot = ((long long)bk * a.n_splits + s) * a.R + row;
     const float inv = lt > 0.f ? 1.0f / lt : 0.f;
     float* orow = a.ws_o + slot * D;
 #pragma unroll

@@ -59,7 +59,7 @@ extern "C" {
                                    negative or not finite, or overlapping output buffers */
 #define FA_ERR_UNSUPPORTED (-2) /* head dim d not in {64, 128} (the bf16 forward entry points
                                    fa_fwd, fa_fwd_gqa and fa_fwd_ext also take 256); split-KV:
-                                   over 32 rows per K/V head */
+                                   over 512 rows per K/V head */
 #define FA_ERR_ALIGNMENT (-3)   /* a pointer is not 16-byte aligned */
 #define FA_ERR_LAUNCH (-4)      /* the kernel launch call (or a HIP runtime query) returned an
                                    error */
@@ -146,14 +146,15 @@ int fa_fwd_ext(const void* q, const void* k, const void* v, void* o, float* lse,
  *
  * fa_splitkv_workspace_bytes -- bytes of device workspace fa_fwd_splitkv needs for this shape and
  *   split count (n_splits = 0: the library's choice, about 768 waves of one (batch, K/V head,
- *   split) each, at least 128 keys per split; a given count is capped at one split per 32 keys).
+ *   split, 32-row tile) each, at least 128 keys per split; a given count is capped at one split
+ *   per 32 keys).
  *   Returns 0 when the shape is not accepted by fa_fwd_splitkv.
  * fa_fwd_splitkv -- bf16 q, k, v, o; fp32 arithmetic; fp32 partial results of every split in
  *   `workspace` (caller-owned device memory of at least fa_splitkv_workspace_bytes(...) bytes,
  *   16-byte aligned, overlapping nothing else; its contents on entry do not matter and are
  *   overwritten). Two kernels are enqueued on `stream`; calls that share a workspace must not
- *   overlap. Limits: N_kv <= 2^22, (H / H_kv) * N_q <= 32 (the query rows that share one K/V head
- *   form one 32-row tile; more return FA_ERR_UNSUPPORTED), d in {64, 128}. Other conventions and
+ *   overlap. Limits: N_kv <= 2^22, (H / H_kv) * N_q <= 512 (the query rows that share one K/V
+ *   head, stacked and cut into 32-row tiles; more return FA_ERR_UNSUPPORTED), d in {64, 128}. Other conventions and
  *   return codes as fa_fwd_gqa; a workspace that is NULL or too small returns FA_ERR_INVALID_ARG.
  */
 size_t fa_splitkv_workspace_bytes(int B, int H, int H_kv, int N_q, int N_kv, int d, int causal,

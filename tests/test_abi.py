@@ -187,8 +187,8 @@ BAD_DEC = [
     (dict(causal=2), fa.FA_ERR_INVALID_ARG),
     (dict(scale=float("nan")), fa.FA_ERR_INVALID_ARG),
     (dict(n_splits=-1), fa.FA_ERR_INVALID_ARG),
-    (dict(Nq=9), fa.FA_ERR_UNSUPPORTED),                  # 4 heads x 9 queries > 32 rows
-    (dict(H=64, H_kv=1), fa.FA_ERR_UNSUPPORTED),         # 64 heads share one K/V head
+    (dict(Nq=129, causal=0), fa.FA_ERR_UNSUPPORTED),      # 4 heads x 129 queries > 512 rows
+    (dict(H=1024, H_kv=1), fa.FA_ERR_UNSUPPORTED),       # 1024 heads share one K/V head
     (dict(d=96), fa.FA_ERR_UNSUPPORTED),
     (dict(ws=W_ + 8), fa.FA_ERR_ALIGNMENT),
     (dict(ws=Q), fa.FA_ERR_INVALID_ARG),                  # workspace overlaps q
@@ -209,7 +209,12 @@ def test_splitkv_workspace_bytes():
     o_part = 2 * splits * R * 128 * 4
     assert n == (o_part + 255) // 256 * 256 + 2 * splits * R * 4
     assert f(1, 8, 2, 1, 4096, 128, 1, 0) > 0          # library's own split count
-    assert f(1, 8, 2, 9, 4096, 128, 1, 0) == 0          # 36 rows per K/V head: not accepted
+    assert f(1, 8, 2, 128, 4096, 128, 1, 0) > 0         # 512 rows per K/V head: the maximum
+    assert f(1, 8, 2, 129, 4096, 128, 1, 0) == 0        # 516 rows per K/V head: not accepted
+    # several row tiles per K/V head take fewer automatic splits (about 768 waves in all)
+    one_tile = f(1, 8, 2, 8, 32768, 128, 1, 0) // (32 * (128 + 1) * 4)
+    four_tiles = f(1, 8, 2, 32, 32768, 128, 1, 0) // (128 * (128 + 1) * 4)
+    assert four_tiles < one_tile
     assert f(1, 8, 3, 1, 4096, 128, 1, 0) == 0          # uneven head groups
     assert f(1, 8, 2, 1, 40, 128, 1, 1000) == f(1, 8, 2, 1, 40, 128, 1, 2)  # at most 1 split / 32 keys
 

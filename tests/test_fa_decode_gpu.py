@@ -5,7 +5,9 @@ Few queries (the last N_q tokens) against N_kv cached keys with grouped K/V head
   * the Llama-3-8B decoding batch at full size (8 sequences x 32 query heads over 8 K/V heads,
     32768 cached keys, d = 128, [B][N][H][d]), every output row against the oracle;
   * ragged key counts (1 key, less than one 32-key step, splits that end mid-step), several
-    queries per sequence, the 32-row limit of a stacked tile (G * N_q = 32), MHA / GQA / MQA,
+    queries per sequence, one full 32-row tile (G * N_q = 32), several tiles per K/V head (ragged
+    G * N_q = 33, 36, 40, 48; 128 = 16 queries x 8 query heads per K/V head; the 512-row
+    maximum), MHA / GQA / MQA,
     d = 64 and 128, both masks, both layouts, automatic and explicit split counts;
   * large scores (a running maximum that moves between splits), scale 0 (uniform weights);
   * bitwise determinism, independence from the split count within the bound, and a workspace
@@ -82,11 +84,24 @@ def test_llama_decode_batch_full_size():
     check(q, k, v, softmax_scale(w["d"]), w["causal"][-1], w["layout"], 0, tag=name)
 
 
-# (N_kv, N_q, H, H_kv): ragged key counts, several queries, 32 stacked rows at most
+def test_llama_decode_sixteen_queries_per_sequence():
+    """Sixteen new tokens per sequence (speculative decoding, chunked prefill): 8 query heads x 16
+    queries = 128 stacked rows per K/V head, four tiles, on the Llama decoding layer's heads and
+    cache length (2 sequences)."""
+    w = dict(B=2, H=32, H_kv=8, N=32768, Nq=16, d=128, dtype="bf16", seed=15)
+    q, k, v = make_inputs(**w)
+    for causal in (True, False):
+        check(q, k, v, softmax_scale(128), causal, "bnhd", 0, tag="llama 16 queries")
+
+
+# (N_kv, N_q, H, H_kv): ragged key counts, several queries, one to sixteen 32-row tiles of
+# stacked rows per K/V head
 _SHAPES = [
     (1, 1, 32, 8), (31, 1, 8, 8), (77, 3, 32, 8), (1000, 8, 32, 8), (5000, 1, 4, 1),
     (33, 3, 8, 8), (4097, 2, 8, 2), (300, 8, 16, 4), (64, 32, 8, 8), (2000, 1, 32, 1),
     (129, 4, 16, 2), (96, 1, 1, 1),
+    (4096, 16, 32, 4), (1000, 5, 16, 2), (77, 9, 32, 8), (33, 33, 8, 8), (700, 48, 4, 4),
+    (3000, 64, 8, 1), (257, 11, 3, 1),
 ]
 
 
@@ -191,7 +206,8 @@ def test_error_codes():
     assert _raw_call(q, k, v, q, lse, B, H, H_kv, Nq, Nkv, d) == fa.FA_ERR_INVALID_ARG  # o aliases q
     assert _raw_call(q, k, v, o, lse, B, H, 3, Nq, Nkv, d) == fa.FA_ERR_INVALID_ARG  # 8 % 3
     assert _raw_call(q, k, v, o, lse, B, H, H_kv, 200, Nkv, d) == fa.FA_ERR_INVALID_ARG  # Nq > Nkv
-    assert _raw_call(q, k, v, o, lse, B, H, H_kv, 9, Nkv, d) == fa.FA_ERR_UNSUPPORTED  # 4 * 9 > 32
+    # 4 query heads x 129 queries > 512 stacked rows (refused before any launch)
+    assert _raw_call(q, k, v, o, lse, B, H, H_kv, 129, Nkv, d, causal=0) == fa.FA_ERR_UNSUPPORTED
     assert _raw_call(q, k, v, o, lse, B, H, H_kv, Nq, Nkv, 96) == fa.FA_ERR_UNSUPPORTED
     assert _raw_call(q, k, v, o, lse, B, H, H_kv, Nq, Nkv, d, layout=5) == fa.FA_ERR_INVALID_ARG
     assert _raw_call(q, k, v, o, lse, B, H, H_kv, Nq, Nkv, d, scale=float("nan")) == \
