@@ -96,7 +96,7 @@ template <int D, bool CAUSAL>
 hipError_t launch_f32(fa::F32Args a, int n_qblk, hipStream_t s) {
   void* args[] = {&a};
   return hipLaunchKernel(reinterpret_cast<const void*>(&fa::fa_fwd_f32_kernel<D, CAUSAL>),
-                         dim3(n_qblk, a.BH), dim3(fa::kF32BlockQ), args, 0, s);
+                         dim3(n_qblk, a.BH), dim3(fa::kF32Threads), args, 0, s);
 }
 
 // ---- score variants and d = 256 ------------------------------------------------------------------
@@ -251,7 +251,7 @@ int run_f32(const float* q, const float* k, const float* v, float* o, float* lse
   a.lse = lse;
   fill_shape(a, B, H, H_kv, N, d, layout);
   a.scale_log2 = scale * fa::kLog2e;
-  const int n_qblk = (N + fa::kF32BlockQ - 1) / fa::kF32BlockQ;
+  const int n_qblk = (N + fa::kF32Rows - 1) / fa::kF32Rows;
   const hipStream_t s = static_cast<hipStream_t>(stream);
   hipError_t e;
   if (d == 128)
