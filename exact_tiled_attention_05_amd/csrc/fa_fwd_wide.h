@@ -428,27 +428,41 @@ __global__ __launch_bounds__(kWideWaves * 64) __attribute__((amdgpu_waves_per_eu
   }
   if (t < n_tiles) run_tile(std::integral_constant<int, 0>{}, t);
 
-  // epilogue: O = a / l, LSE = ln 2 (m + log2 l)
-  auto store = [&](WideBlock& x, int row0) __attribute__((always_inline)) {
+  // epilogue: O = a / l, LSE = ln 2 (m + log2 l). O goes out through LDS, whose K/V stages are
+  // free once every wave is past its last tile: each wave writes its 64 rows of bf16 O into a
+  // swizzled 16 KB region (the tile layout of the K/V stages) and reads them back as whole
+  // 256-byte rows, so every store instruction writes 4 complete rows instead of 16 bytes of each
+  // of 32 rows. The loads of the two tiles past the last one (zero-size: they only write zeros
+  // into the stages) may still be in flight; they land before the barrier.
+  wait_dma();
+  __syncthreads();
+  char* const so = (wave < 2 ? &sK[0][0] : &sV[0][0]) + (wave & 1) * (64 * 256);
+  auto stage_out = [&](WideBlock& x, int r0) __attribute__((always_inline)) {
     const float lt = half_swap_sum(x.l);
-    const int qrow = row0 + c;
-    if (qrow < N) {
-      const float inv = lt > 0.f ? 1.0f / lt : 0.f;
-      bf16* orow = a.o + qh + (long long)qrow * a.q_rs;
+    const float inv = lt > 0.f ? 1.0f / lt : 0.f;
+    const int r = r0 + c;
 #pragma unroll
-      for (int db = 0; db < DB; db++)
+    for (int db = 0; db < DB; db++)
 #pragma unroll
-        for (int g4 = 0; g4 < 4; g4++) {
-          bf16x4 ov;
+      for (int g4 = 0; g4 < 4; g4++) {
+        bf16x4 ov;
 #pragma unroll
-          for (int e = 0; e < 4; e++) ov[e] = (bf16)(x.o[db][4 * g4 + e] * inv);
-          *reinterpret_cast<bf16x4*>(orow + 32 * db + 8 * g4 + 4 * h) = ov;
-        }
-      if (h == 0) a.lse[(long long)bh * N + qrow] = lt > 0.f ? kLn2 * (x.m2 + fast_log2(lt)) : -INFINITY;
-    }
+        for (int e = 0; e < 4; e++) ov[e] = (bf16)(x.o[db][4 * g4 + e] * inv);
+        *(FA_LDS bf16x4*)((FA_LDS char*)so + S::off(r, 4 * db + g4) + 8 * h) = ov;
+      }
+    const int qrow = ra + r;
+    if (h == 0 && qrow < N)
+      a.lse[(long long)bh * N + qrow] = lt > 0.f ? kLn2 * (x.m2 + fast_log2(lt)) : -INFINITY;
   };
-  store(A, ra);
-  store(B, rb);
+  stage_out(A, 0);
+  stage_out(B, 32);
+#pragma unroll
+  for (int it = 0; it < 16; it++) {
+    const int r = 4 * it + (lane >> 4), j = lane & 15;
+    const bf16x8 ov = *(const FA_LDS bf16x8*)((FA_LDS char*)so + S::off(r, j));
+    const int qrow = ra + r;
+    if (qrow < N) *reinterpret_cast<bf16x8*>(a.o + qh + (long long)qrow * a.q_rs + 8 * j) = ov;
+  }
 }
 
 }  // namespace fa

@@ -66,7 +66,7 @@ FWD_CASES = [
     # name, dict(B, H, H_kv, N, d, causal, layout, extra make_inputs args)
     ("wide_llama_n8k_causal", dict(B=1, H=8, H_kv=8, N=8192, d=128, causal=True, layout="bhnd")),
     ("wide_gqa_n8k_causal_bnhd", dict(B=1, H=8, H_kv=2, N=8192, d=128, causal=True, layout="bnhd")),
-    ("wide_n32k_causal", dict(B=1, H=2, H_kv=2, N=32768, d=128, causal=True, layout="bhnd")),
+    ("wide_n32k_causal", dict(B=1, H=16, H_kv=16, N=32768, d=128, causal=True, layout="bhnd")),
     ("wide_ragged_noncausal", dict(B=2, H=3, H_kv=3, N=4097 + 63, d=128, causal=False,
                                    layout="bhnd")),
     ("ext_outlier_n2k", dict(B=2, H=32, H_kv=32, N=2048, d=128, causal=False, layout="bhnd",
