@@ -26,7 +26,8 @@
 //         P3  S_A(j+1) = K(j+1) Q_A^T       | B, step j: exponentials, bf16 P, pair sums
 //         P4  O_B     += V(j)^T P_B(j)^T    | B's row sum; A, step j+1: shifted scores, maximum
 //     Each phase is written as 8 groups of one MFMA and the vector instructions that fit in its
-//     32 cycles, pinned in place (see pin()). V(j) is read from LDS in P1, K(j+1) in P2.
+//     32 cycles, pinned in place (see pin()). K(j+1) is read from LDS in P2, V(j+1) in P4 (into
+//     the second of two V fragment sets, so that no phase waits for V it has just requested).
 //   * Exponentials are taken relative to the current reference; the check that moves it (some
 //     shifted score above the slack, or the row's first visible score) follows the shift, so the
 //     rare rescale of the accumulator is a wave-uniform branch between phases, before the
@@ -34,8 +35,8 @@
 //     the end of the sequence.
 //   * K/V tiles of 64 keys (two steps) go straight from memory into two swizzled LDS stages by
 //     16-byte DMA, one barrier per tile, between P1 and P2 of its second step: the last read of
-//     tile t (V of its second step, P1) precedes it and the first read of tile t+1 (K of the next
-//     step, P2) follows it. The DMA pieces of tile t+2 are issued one per MFMA group of that P2.
+//     tile t (V of its second step, P4 of its first step) precedes it and the first reads of tile
+//     t+1 (K of the next step, P2; V of the next step, P4) follow it. The DMA pieces of tile t+2 are issued one per MFMA group of that P2.
 //   * Every wave runs every step of its workgroup's key range, so the barrier counts match; the
 //     steps past a block's causal diagonal (or past N) are fully masked, which makes their
 //     probabilities 0 and leaves the running state unchanged. The workgroup's step count is
@@ -343,6 +344,7 @@ __global__ __launch_bounds__(kWideWaves * 64) __attribute__((amdgpu_waves_per_eu
 
   bf16x8 kf[DK];
   bf16x8 vf[DB][2];
+  bf16x8 vf2[DB][2];  // V fragments of odd steps (vf: even steps), each read in P4 of the step before
   auto load_k = [&](const char* tile, int r) __attribute__((always_inline)) {
 #pragma unroll
     for (int dk = 0; dk < DK; dk++) kf[dk] = tile_row_at<D>(tile, lo_, r, dk);
@@ -359,6 +361,8 @@ __global__ __launch_bounds__(kWideWaves * 64) __attribute__((amdgpu_waves_per_eu
   race_check_drain();
   __syncthreads();
   load_k(sK[0], 0);
+#pragma unroll
+  for (int i = 0; i < 8; i++) vf[i & 3][i >> 2] = tile_tr_at<D>(sV[0], lo_, 16 * (i >> 2), i & 3);
   {
     f32x16 s0 = f32x16{};
 #pragma unroll
@@ -374,11 +378,11 @@ __global__ __launch_bounds__(kWideWaves * 64) __attribute__((amdgpu_waves_per_eu
   auto step = [&](auto st_c, auto sb_c, int t) __attribute__((always_inline)) {
     constexpr int st = decltype(st_c)::value, sb = decltype(sb_c)::value;
     const int k0 = t * TK + 32 * sb;
-    // P1: V(j) requested; S_B(j) = K(j) Q_B^T; probabilities of A, step j
-    phase_exp(B, kf, A, [&](int i) __attribute__((always_inline)) {
-      vf[i & 3][i >> 2] = tile_tr_at<D>(sV[st], lo_, 32 * sb + 16 * (i >> 2), i & 3);
-    });
     constexpr bool LAST = sb == SPT - 1;  // last step of tile t
+    auto& vcur = (sb & 1) ? vf2 : vf;
+    auto& vnext = (sb & 1) ? vf : vf2;
+    // P1: S_B(j) = K(j) Q_B^T; probabilities of A, step j
+    phase_exp(B, kf, A, [](int) {});
     i32x4v rk, rv;
     if constexpr (LAST) {
       // tile t + 1 in LDS for every wave (each waits for its own pieces, then the barrier)
@@ -388,7 +392,7 @@ __global__ __launch_bounds__(kWideWaves * 64) __attribute__((amdgpu_waves_per_eu
     }
     // P2: K(j+1) requested (and, in a tile's last step, the DMA of tile t + 2); O_A += V(j)^T
     // P_A(j)^T, A's sum; B's scores shifted and checked
-    phase_pv(A, vf, B, sl2, [&](int i) __attribute__((always_inline)) {
+    phase_pv(A, vcur, B, sl2, [&](int i) __attribute__((always_inline)) {
       kf[i] = sb < SPT - 1 ? tile_row_at<D>(sK[st], lo_, 32 * (sb + 1), i)
                            : tile_row_at<D>(sK[st ^ 1], lo_, 0, i);
       if constexpr (LAST) {
@@ -408,7 +412,12 @@ __global__ __launch_bounds__(kWideWaves * 64) __attribute__((amdgpu_waves_per_eu
     phase_exp(A, kf, B, [](int) {});
     // P4: O_B += V(j)^T P_B(j)^T, B's sum; A's scores of step j + 1 shifted and checked (past the
     // last step: garbage, fully masked)
-    phase_pv(B, vf, A, sl2, [](int) {});
+    phase_pv(B, vcur, A, sl2, [&](int i) __attribute__((always_inline)) {
+      // V(j+1): the next step of this tile, or the first of tile t + 1 (visible since this step's
+      // barrier; past the last tile the reads see a stage nothing uses)
+      vnext[i & 3][i >> 2] = LAST ? tile_tr_at<D>(sV[st ^ 1], lo_, 16 * (i >> 2), i & 3)
+                                  : tile_tr_at<D>(sV[st], lo_, 32 * (sb + 1) + 16 * (i >> 2), i & 3);
+    });
     if (__builtin_expect(k0 + 63 > edgeA, 0)) wide_mask(A, k0 + 32, lastA, h);
     wide_check(A);
   };
