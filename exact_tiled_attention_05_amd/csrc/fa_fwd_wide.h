@@ -37,10 +37,10 @@
 //     16-byte DMA, one barrier per tile, between P1 and P2 of its second step: the last read of
 //     tile t (V of its second step, P4 of its first step) precedes it and the first reads of tile
 //     t+1 (K of the next step, P2; V of the next step, P4) follow it. The DMA pieces of tile t+2 are issued one per MFMA group of that P2.
-//   * Every wave runs every step of its workgroup's key range, so the barrier counts match; the
-//     steps past a block's causal diagonal (or past N) are fully masked, which makes their
-//     probabilities 0 and leaves the running state unchanged. The workgroup's step count is
-//     rounded up to whole tiles the same way.
+//   * Every wave takes part in every tile of its workgroup's key range, so the barrier counts
+//     match. The steps past a block's causal diagonal (or past N) are fully masked, which makes
+//     their probabilities 0 and leaves the running state unchanged; once a whole tile is past both
+//     of a wave's blocks, the wave only meets the tile's barrier and issues its loads.
 #pragma once
 
 #include "fa_tiles.h"
@@ -430,12 +430,36 @@ __global__ __launch_bounds__(kWideWaves * 64) __attribute__((amdgpu_waves_per_eu
       one(std::integral_constant<int, 3>{});
     }
   };
+  // Tiles past the last key any row of this wave sees (the causal diagonal of its block B, or N)
+  // are fully masked for both blocks and change nothing: the wave only takes part in their barrier
+  // and loads. n_real is wave-uniform; every wave still meets one barrier per tile.
+  const int last_seen = min(N - 1, CAUSAL ? rb + 31 : N - 1);
+  const int n_real = min(n_tiles, last_seen / TK + 1);
+  auto idle_tile = [&](auto st_c, int tt) __attribute__((always_inline)) {
+    constexpr int st = decltype(st_c)::value;
+    wait_dma();
+    __syncthreads();
+    i32x4v rk, rv;
+    tile_rsrc2(tt + 2, rk, rv);
+#pragma unroll
+    for (int i = 0; i < WideDma<TK, NS>::PW; i++) dma.piece(st, 0, i, rk);
+#pragma unroll
+    for (int i = 0; i < WideDma<TK, NS>::PW; i++) dma.piece(st, 1, i, rv);
+    race_check_drain();
+  };
   int t = 0;
-  for (; t + 1 < n_tiles; t += 2) {
+  for (; t + 1 < n_real; t += 2) {
     run_tile(std::integral_constant<int, 0>{}, t);
     run_tile(std::integral_constant<int, 1>{}, t + 1);
   }
-  if (t < n_tiles) run_tile(std::integral_constant<int, 0>{}, t);
+  if (t < n_real) {
+    run_tile(std::integral_constant<int, 0>{}, t);
+    t++;
+  }
+  for (; t < n_tiles; t++) {
+    if (t & 1) idle_tile(std::integral_constant<int, 1>{}, t);
+    else idle_tile(std::integral_constant<int, 0>{}, t);
+  }
 
   // epilogue: O = a / l, LSE = ln 2 (m + log2 l). O goes out through LDS, whose K/V stages are
   // free once every wave is past its last tile: each wave writes its 64 rows of bf16 O into a
