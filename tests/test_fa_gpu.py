@@ -132,6 +132,17 @@ def test_ragged_bf16(N, d, causal):
     _check(f"ragged bf16 N={N} d={d}", q, k, v, W.softmax_scale(d), causal)
 
 
+@pytest.mark.parametrize("N", [4096, 4097, 4351, 5000, 8191])
+@pytest.mark.parametrize("causal", [False, True])
+def test_ragged_wide_rows(N, causal):
+    """d = 128 with N >= 4096 runs the wide-row kernel (256-row workgroups, 64-key tiles, waves
+    that go idle past their blocks' diagonal): lengths that end inside a tile, a workgroup and a
+    wave's block, every head on every boundary row and on sampled rows."""
+    q, k, v = W.make_inputs(1, 3, N, 128, "bf16", seed=N + causal)
+    rows = _boundary_rows(N, W.sampled_rows(N, 48, seed=N).numpy())
+    _check("wide N=%d" % N, q, k, v, W.softmax_scale(128), causal, rows=rows)
+
+
 @pytest.mark.parametrize("N", [1, 77, 300])
 @pytest.mark.parametrize("d", [64, 128])
 @pytest.mark.parametrize("causal", [False, True])
