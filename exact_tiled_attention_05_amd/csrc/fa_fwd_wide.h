@@ -8,13 +8,13 @@
 //     m' = max(m, rowmax(S)),  alpha = 2^(m - m'),  p = 2^(s - m'),  l' = alpha l + sum p,
 //     a' = alpha a + p V,
 // with O = a / l and LSE = m + log l (natural-log units on output) written once at the end. The
-// reference moves lazily (only when a score exceeds it by more than kRescaleSlack in log2 units,
+// reference moves lazily (only when a score exceeds it by more than kWideSlack in log2 units,
 // as in the other kernels), with the -inf guard of "Online Softmax & FlashAttention", Listing
 // 26.3 for rows that have seen no key yet.
 //
 // What is different here is the shape of the work per wave and the instruction stream.
 //   * A wave owns 64 query rows as two independent 32-row blocks A and B (a workgroup is 4 waves,
-//     256 rows, one wave per SIMD: about 360 registers per lane). Every K and V operand fragment
+//     256 rows, one wave per SIMD: about 370 registers per lane). Every K and V operand fragment
 //     read from LDS feeds one MFMA of each block, so a wave reads 0.5 KB of LDS per 32x32x16 MFMA
 //     instead of 1 KB, and the workgroup refills its K/V tiles from L2 half as often per query
 //     row as a 128-row one.
@@ -36,7 +36,8 @@
 //   * K/V tiles of 64 keys (two steps) go straight from memory into two swizzled LDS stages by
 //     16-byte DMA, one barrier per tile, between P1 and P2 of its second step: the last read of
 //     tile t (V of its second step, P4 of its first step) precedes it and the first reads of tile
-//     t+1 (K of the next step, P2; V of the next step, P4) follow it. The DMA pieces of tile t+2 are issued one per MFMA group of that P2.
+//     t+1 (K of the next step, P2; V of the next step, P4) follow it. The DMA pieces of tile t+2
+//     are issued one per MFMA group of that P2. The epilogue stores O through LDS as whole rows.
 //   * Every wave takes part in every tile of its workgroup's key range, so the barrier counts
 //     match. The steps past a block's causal diagonal (or past N) are fully masked, which makes
 //     their probabilities 0 and leaves the running state unchanged; once a whole tile is past both
