@@ -59,6 +59,7 @@
 #include <type_traits>
 
 #include "fa_device.h"
+#include "fa_tiles.h"
 
 namespace fa {
 
@@ -415,21 +416,34 @@ __global__ __launch_bounds__(kNumWaves * 64) void fa_fwd_bf16_kernel(Bf16Args a)
     tile(I2{}, j + 2);
   }
 
-  // Epilogue: O = a / l, LSE = ln2 * (m + log2 l).
+  // Epilogue: O = a / l, LSE = ln2 * (m + log2 l). O goes out through LDS (the tile stages, free
+  // once every wave is past the last tile): each wave writes its 32 rows of bf16 O into a swizzled
+  // region of its own and reads them back as whole rows, so a store instruction writes complete
+  // rows instead of 16 bytes of 32 rows.
   const float lt = half_swap_sum(st.l);
-  if (L.qrow < N) {
-    const float inv = 1.0f / lt;
-    bf16* orow = a.o + qhead + (long long)L.qrow * a.q_rs;
+  const float inv = lt > 0.f ? 1.0f / lt : 0.f;
+  using SO = Swz<D>;
+  constexpr int OREG = 32 * SO::ROW;  // one wave's 32 rows
+  static_assert(2 * OREG <= Layout<D>::K_BYTES && 2 * OREG <= Layout<D>::V_BYTES, "O staging fits");
+  __syncthreads();
+  char* const so = (wave < 2 ? sK0 : wave < 4 ? sK1 : wave < 6 ? sK2 : sV0) + (wave & 1) * OREG;
 #pragma unroll
-    for (int db = 0; db < DB; db++)
+  for (int db = 0; db < DB; db++)
 #pragma unroll
-      for (int g4 = 0; g4 < 4; g4++) {
-        bf16x4 ov;
+    for (int g4 = 0; g4 < 4; g4++) {
+      bf16x4 ov;
 #pragma unroll
-        for (int e = 0; e < 4; e++) ov[e] = (bf16)(st.acc[db][4 * g4 + e] * inv);
-        *reinterpret_cast<bf16x4*>(orow + 32 * db + 8 * g4 + 4 * L.h) = ov;
-      }
-    if (L.h == 0) a.lse[(size_t)bh * N + L.qrow] = kLn2 * (st.m2 + fast_log2(lt));
+      for (int e = 0; e < 4; e++) ov[e] = (bf16)(st.acc[db][4 * g4 + e] * inv);
+      *(FA_LDS bf16x4*)((FA_LDS char*)so + SO::off(L.c, 4 * db + g4) + 8 * L.h) = ov;
+    }
+  if (L.qrow < N && L.h == 0) a.lse[(size_t)bh * N + L.qrow] = kLn2 * (st.m2 + fast_log2(lt));
+  constexpr int RPI = 64 / SO::CPR;  // rows per read instruction
+#pragma unroll
+  for (int it = 0; it < 32 / RPI; it++) {
+    const int r = RPI * it + lane / SO::CPR, j = lane % SO::CPR;
+    const bf16x8 ov = *(const FA_LDS bf16x8*)((FA_LDS char*)so + SO::off(r, j));
+    const int row = L.qw0 + r;
+    if (row < N) *reinterpret_cast<bf16x8*>(a.o + qhead + (long long)row * a.q_rs + 8 * j) = ov;
   }
 }
 
