@@ -206,17 +206,28 @@ __global__ __launch_bounds__(kBwdQWaves * 64) __attribute__((amdgpu_waves_per_eu
     if (j + 1 < n_kt) tile(std::integral_constant<int, 1>{}, j + 1);
   }
 
-  if (qrow < N) {
-    bf16* dst = a.dq + qoff;
+  // dQ goes out through LDS (the K/V stages, free once every wave is past the last tile): each
+  // wave writes its 32 rows into a swizzled region of its own and reads them back as whole rows.
+  constexpr int OREG = 32 * S::ROW;  // one wave's 32 rows
+  static_assert(kBwdQWaves * OREG <= (int)sizeof(sK2), "dQ staging fits");
+  __syncthreads();
+  char* const so = &sK2[0][0] + wave * OREG;
 #pragma unroll
-    for (int db = 0; db < DB; db++)
+  for (int db = 0; db < DB; db++)
 #pragma unroll
-      for (int g4 = 0; g4 < 4; g4++) {
-        bf16x4 v4;
+    for (int g4 = 0; g4 < 4; g4++) {
+      bf16x4 v4;
 #pragma unroll
-        for (int e = 0; e < 4; e++) v4[e] = (bf16)(acc[db][4 * g4 + e] * a.scale);
-        *reinterpret_cast<bf16x4*>(dst + 32 * db + 8 * g4 + 4 * h) = v4;
-      }
+      for (int e = 0; e < 4; e++) v4[e] = (bf16)(acc[db][4 * g4 + e] * a.scale);
+      *(FA_LDS bf16x4*)((FA_LDS char*)so + S::off(c, 4 * db + g4) + 8 * h) = v4;
+    }
+  constexpr int RPI = 64 / S::CPR;  // rows per read instruction
+#pragma unroll
+  for (int it = 0; it < 32 / RPI; it++) {
+    const int r = RPI * it + lane / S::CPR, j = lane % S::CPR;
+    const bf16x8 v8 = *(const FA_LDS bf16x8*)((FA_LDS char*)so + S::off(r, j));
+    const int row = qw0 + r;
+    if (row < N) *reinterpret_cast<bf16x8*>(a.dq + b * a.q_bs + hq * a.q_hs + (long long)row * a.q_rs + 8 * j) = v8;
   }
 }
 
