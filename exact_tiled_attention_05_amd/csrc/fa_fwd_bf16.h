@@ -340,11 +340,29 @@ __global__ __launch_bounds__(kNumWaves * 64) void fa_fwd_bf16_kernel(Bf16Args a)
   TileRegs<D> stage;
   load_tile<D>(src, 0, N, wave, stage);
   WaveState<D> st;
+  {
+    // Q of the wave's 32 rows: whole-row loads (4 rows per instruction), through a wave-private
+    // swizzled LDS region of stage 1 or 2 (not written before the first crossing, which follows
+    // the prologue barrier) into the operand layout
+    using SQ = Swz<D>;
+    char* const sq = (wave < 2 ? sK1 : wave < 4 ? sK2 : wave < 6 ? sV1 : sV2) + (wave & 1) * (32 * SQ::ROW);
+    constexpr int RPI = 64 / SQ::CPR;
+    bf16x8 qr[32 / RPI];
 #pragma unroll
-  for (int dk = 0; dk < DK; dk++)
-    st.qf[dk] = (L.qrow < N)
-                    ? *reinterpret_cast<const bf16x8*>(Qh + (long long)L.qrow * a.q_rs + dk * 16 + L.h * 8)
-                    : bf16x8{};
+    for (int it = 0; it < 32 / RPI; it++) {
+      const int r = RPI * it + lane / SQ::CPR, j = lane % SQ::CPR;
+      qr[it] = L.qw0 + r < N ? *reinterpret_cast<const bf16x8*>(Qh + (long long)(L.qw0 + r) * a.q_rs + 8 * j)
+                             : bf16x8{};
+    }
+#pragma unroll
+    for (int it = 0; it < 32 / RPI; it++) {
+      const int r = RPI * it + lane / SQ::CPR, j = lane % SQ::CPR;
+      *(FA_LDS bf16x8*)((FA_LDS char*)sq + SQ::off(r, j)) = qr[it];
+    }
+#pragma unroll
+    for (int dk = 0; dk < DK; dk++)
+      st.qf[dk] = *(const FA_LDS bf16x8*)((FA_LDS char*)sq + SQ::off(L.c, 2 * dk + L.h));
+  }
 #pragma unroll
   for (int db = 0; db < DB; db++) st.acc[db] = f32x16{};
   st.m2 = -INFINITY;
