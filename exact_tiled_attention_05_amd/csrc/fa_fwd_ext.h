@@ -339,34 +339,53 @@ __global__ __launch_bounds__(kExtWaves * 64) __attribute__((amdgpu_waves_per_eu(
     if (t + 1 <= t_last) tile(std::integral_constant<int, 1>{}, t + 1);
   }
 
-  // O goes out through LDS (the K/V stages, free once every wave is past the last tile): each
-  // wave writes its 32 rows of bf16 O into a swizzled region of its own and reads them back as
-  // whole rows, so a store instruction writes complete rows instead of 16 bytes of 32 rows.
   const float lt = half_swap_sum(l);
   const float inv = lt > 0.f ? 1.0f / lt : 0.f;
-  __syncthreads();
-  constexpr int OREG = 32 * S::ROW;  // one wave's 32 rows
-  static_assert(2 * OREG <= (int)sizeof(sK2) && 2 * OREG <= (int)sizeof(sV2), "O staging fits");
-  char* const so = (wave < 2 ? &sK2[0][0] : &sV2[0][0]) + (wave & 1) * OREG;
+  if constexpr (ALIBI) {
+    // stored straight from the accumulator: the staging below takes the ALiBi kernel past the
+    // register count of three waves per SIMD (166 -> 189 at d = 128), which costs more than the
+    // stores gain
+    if (qrow < N) {
+      bf16* orow = a.o + qoff;
 #pragma unroll
-  for (int db = 0; db < DB; db++)
+      for (int db = 0; db < DB; db++)
 #pragma unroll
-    for (int g4 = 0; g4 < 4; g4++) {
-      bf16x4 ov;
+        for (int g4 = 0; g4 < 4; g4++) {
+          bf16x4 ov;
 #pragma unroll
-      for (int e = 0; e < 4; e++) ov[e] = (bf16)(acc[db][4 * g4 + e] * inv);
-      *(FA_LDS bf16x4*)((FA_LDS char*)so + S::off(c, 4 * db + g4) + 8 * h) = ov;
+          for (int e = 0; e < 4; e++) ov[e] = (bf16)(acc[db][4 * g4 + e] * inv);
+          *reinterpret_cast<bf16x4*>(orow + 32 * db + 8 * g4 + 4 * h) = ov;
+        }
+      if (h == 0) a.lse[(long long)bh * N + qrow] = lt > 0.f ? kLn2 * (m2 + fast_log2(lt)) : -INFINITY;
     }
-  if (qrow < N && h == 0)
-    a.lse[(long long)bh * N + qrow] = lt > 0.f ? kLn2 * (m2 + fast_log2(lt)) : -INFINITY;
-  constexpr int RPI = 64 / S::CPR;  // rows per read instruction
+  } else {
+    // O goes out through LDS (the K/V stages, free once every wave is past the last tile): each
+    // wave writes its 32 rows of bf16 O into a swizzled region of its own and reads them back as
+    // whole rows, so a store instruction writes complete rows instead of 16 bytes of 32 rows.
+    __syncthreads();
+    constexpr int OREG = 32 * S::ROW;  // one wave's 32 rows
+    static_assert(2 * OREG <= (int)sizeof(sK2) && 2 * OREG <= (int)sizeof(sV2), "O staging fits");
+    char* const so = (wave < 2 ? &sK2[0][0] : &sV2[0][0]) + (wave & 1) * OREG;
 #pragma unroll
-  for (int it = 0; it < 32 / RPI; it++) {
-    const int r = RPI * it + lane / S::CPR, j = lane % S::CPR;
-    const bf16x8 ov = *(const FA_LDS bf16x8*)((FA_LDS char*)so + S::off(r, j));
-    const int row = wq0 + r;
-    if (row < N)
-      *reinterpret_cast<bf16x8*>(a.o + b * a.q_bs + hq * a.q_hs + (long long)row * a.q_rs + 8 * j) = ov;
+    for (int db = 0; db < DB; db++)
+#pragma unroll
+      for (int g4 = 0; g4 < 4; g4++) {
+        bf16x4 ov;
+#pragma unroll
+        for (int e = 0; e < 4; e++) ov[e] = (bf16)(acc[db][4 * g4 + e] * inv);
+        *(FA_LDS bf16x4*)((FA_LDS char*)so + S::off(c, 4 * db + g4) + 8 * h) = ov;
+      }
+    if (qrow < N && h == 0)
+      a.lse[(long long)bh * N + qrow] = lt > 0.f ? kLn2 * (m2 + fast_log2(lt)) : -INFINITY;
+    constexpr int RPI = 64 / S::CPR;  // rows per read instruction
+#pragma unroll
+    for (int it = 0; it < 32 / RPI; it++) {
+      const int r = RPI * it + lane / S::CPR, j = lane % S::CPR;
+      const bf16x8 ov = *(const FA_LDS bf16x8*)((FA_LDS char*)so + S::off(r, j));
+      const int row = wq0 + r;
+      if (row < N)
+        *reinterpret_cast<bf16x8*>(a.o + b * a.q_bs + hq * a.q_hs + (long long)row * a.q_rs + 8 * j) = ov;
+    }
   }
 }
 
