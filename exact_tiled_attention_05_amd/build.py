@@ -31,10 +31,13 @@ HIP_FLAGS = [
 # Translation units of the library and the extra flags of each. The wide-row forward kernel needs
 # about 360 registers per lane; with its MFMA results forced into VGPRs the Q operands go to AGPRs
 # (read directly by the MFMAs) instead of the accumulators the softmax reads and rescales. The
-# flag is kept to that file so that it changes no other kernel.
+# flag is kept to that file so that it changes no other kernel. The wide dK/dV kernel of the
+# backward pass has its own file too: it keeps the compiler's default form (its accumulators in
+# AGPRs) and writes out the MFMAs whose results belong in VGPRs.
 SOURCES = [
     ("fa_api.hip", []),
     ("fa_wide.hip", ["-mllvm", "-amdgpu-mfma-vgpr-form"]),
+    ("fa_bwd_wide.hip", []),
 ]
 
 

@@ -17,8 +17,9 @@
 #include "fa_fwd_wide.h"
 
 namespace fa {
-// fa_wide.hip (compiled separately, see there)
+// fa_wide.hip and fa_bwd_wide.hip (compiled separately, see there)
 hipError_t launch_wide(const WideArgs& args, bool causal, hipStream_t stream);
+hipError_t launch_bwd_dkdv_wide(const BwdArgs& args, bool causal, hipStream_t stream);
 }  // namespace fa
 
 namespace {
@@ -446,8 +447,13 @@ hipError_t launch_bwd(fa::BwdArgs a, hipStream_t s) {
   hipError_t e = hipLaunchKernel(reinterpret_cast<const void*>(&fa::fa_bwd_dq_kernel<D, CAUSAL>),
                                  dim3(a.n_qblk * a.BH), dim3(fa::kBwdQWaves * 64), args, 0, s);
   if (e != hipSuccess) return e;
-  e = hipLaunchKernel(reinterpret_cast<const void*>(&fa::fa_bwd_dkdv_kernel<D, CAUSAL>),
-                      dim3(a.n_kblk * a.BHkv * a.hsplit), dim3(fa::kBwdKvWaves * 64), args, 0, s);
+  // dK/dV: at d = 128 the wide kernel (fa_bwd_wide.h: 4 waves of 64 keys, bit-identical results),
+  // at d = 64 the 8-wave one
+  if constexpr (D == 128)
+    e = fa::launch_bwd_dkdv_wide(a, CAUSAL, s);
+  else
+    e = hipLaunchKernel(reinterpret_cast<const void*>(&fa::fa_bwd_dkdv_kernel<D, CAUSAL>),
+                        dim3(a.n_kblk * a.BHkv * a.hsplit), dim3(fa::kBwdKvWaves * 64), args, 0, s);
   if (e != hipSuccess || a.hsplit == 1) return e;
   const long long n4 = (long long)a.BHkv * a.N * (D / 4);
   return hipLaunchKernel(reinterpret_cast<const void*>(&fa::fa_bwd_combine_kernel<D>),

@@ -96,6 +96,15 @@ __device__ __forceinline__ float sum16(const float (&p)[16]) {
   return (t[0] + t[1]) + (t[2] + t[3]);
 }
 
+// Hand-ordered instruction streams (the kernels with one wave per SIMD): an empty asm that names a
+// value emits nothing and, unlike a real use, makes the compiler wait for nothing, but keeps it
+// from moving the instruction that produces the value past that point (to its first use); a
+// scheduling barrier closes a group of instructions.
+__device__ __forceinline__ void pin(const f32x16& x) { asm volatile("" ::"v"(x)); }
+__device__ __forceinline__ void pin(const bf16x8& x) { asm volatile("" ::"v"(x)); }
+__device__ __forceinline__ void pin(float x) { asm volatile("" ::"v"(x)); }
+__device__ __forceinline__ void fence() { __builtin_amdgcn_sched_barrier(0); }
+
 __device__ inline float fast_exp2(float x) { return __builtin_amdgcn_exp2f(x); }
 __device__ inline float fast_log2(float x) { return __builtin_amdgcn_logf(x); }
 

@@ -124,13 +124,8 @@ __device__ __forceinline__ void wide_check(WideBlock& x) {
 
 // Instruction order. A wave is alone on its SIMD, so the order of its instructions decides how
 // much vector work runs under the matrix core's MFMAs. Each phase is written as 8 groups of one
-// MFMA and the vector instructions that fit in its 32 cycles; an empty asm that names the group's
-// results (which emits nothing and, unlike a real use, makes the compiler wait for nothing) keeps
-// the compiler from moving them to their first use, and a scheduling barrier closes the group.
-__device__ __forceinline__ void pin(const f32x16& x) { asm volatile("" ::"v"(x)); }
-__device__ __forceinline__ void pin(const bf16x8& x) { asm volatile("" ::"v"(x)); }
-__device__ __forceinline__ void pin(float x) { asm volatile("" ::"v"(x)); }
-__device__ __forceinline__ void fence() { __builtin_amdgcn_sched_barrier(0); }
+// MFMA and the vector instructions that fit in its 32 cycles, each value pinned in its group and
+// the group closed by a scheduling barrier (pin() and fence(), fa_device.h).
 
 // Exponential phase: S_Y = K Q_Y^T (a chain of 8 MFMAs) with the probabilities of block X: per
 // group two exponentials, and the bf16 packing and pair sum of the previous group's two. load(i)

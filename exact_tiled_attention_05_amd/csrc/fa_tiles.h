@@ -15,6 +15,7 @@ namespace fa {
 
 typedef unsigned int u32x4v __attribute__((ext_vector_type(4)));
 typedef float f32x4v __attribute__((ext_vector_type(4)));
+typedef float f32x2v __attribute__((ext_vector_type(2)));
 
 // Swizzled tile geometry for head dim D (see the header comment).
 template <int D>
