@@ -444,7 +444,8 @@ def bench_variant(args, w):
 
 
 def bench_backward(args, w):
-    """Backward workloads: one step = one fa_bwd call (the dQ kernel, then the dK/dV kernel), with
+    """Backward workloads: one step = one fa_bwd call (the dQ kernel, then the dK/dV kernel, then
+    with query-head splits the kernel that adds the partial dK/dV sums), with
     O and the logsumexp from one forward call and the workspace allocated before the timed
     region. Reported in TFLOP/s of the five gradient products (10*B*H*N^2*d, halved if causal)."""
     import numpy as np
@@ -487,7 +488,9 @@ def bench_backward(args, w):
         "data": "synthetic (seeded N(0,1) Q, K, V, dO)",
         "config": {"workload": args.workload, "B": B, "H": H, "H_kv": H_kv, "N": N, "d": d,
                    "causal": causal, "layout": layout,
-                   "kernel": "fa_bwd (fa_bwd_dq_kernel + fa_bwd_dkdv_kernel)",
+                   "kernel": "fa_bwd (fa_bwd_dq_kernel + fa_bwd_dkdv_wide_kernel at d = 128, "
+                             "fa_bwd_dkdv_kernel at d = 64; + fa_bwd_combine_kernel with "
+                             "query-head splits)",
                    "workspace_bytes": need},
         "roofline": {"bound": "mfma", "achieved": round(tflops, 2), "peak": PEAK_BF16_TFLOPS,
                      "unit": "TFLOP/s", "frac": round(tflops / PEAK_BF16_TFLOPS, 4),
@@ -525,7 +528,7 @@ _FAMILY_SOURCES = {
     "wide": ("fa_fwd_wide.h", "fa_wide.hip", "fa_tiles.h"),
     "ext": ("fa_fwd_ext.h", "fa_tiles.h", "fa_fwd_bf16.h"),
     "decode": ("fa_decode.h",),
-    "bwd": ("fa_bwd.h", "fa_tiles.h"),
+    "bwd": ("fa_bwd.h", "fa_bwd_wide.h", "fa_bwd_wide.hip", "fa_tiles.h"),
 }
 
 

@@ -423,13 +423,17 @@ int run_splitkv(const void* q, const void* k, const void* v, void* o, float* lse
 // ---- backward ----------------------------------------------------------------------------------
 
 // Query-head splits of the dK/dV kernel: enough (K/V head, key block, split) workgroups for about
-// four per CU, a divisor of the group size. MHA, and grouped heads with many K/V heads or long
-// sequences, need none; the Llama-3-8B layer (8 K/V heads, 32 key blocks) takes 4.
-int bwd_hsplit(int B, int H, int H_kv, int N) {
+// four per CU with the 8-wave kernel (d = 64), two per CU with the wide one (d = 128: fewer,
+// longer workgroups balance as well, and every split adds a partial dK/dV to write and add up), a
+// divisor of the group size. MHA, and grouped heads with many K/V heads or long sequences, need
+// none; the grouped Llama-3-8B layer (8 K/V heads, 32 key blocks) takes 2 (measured against 4:
+// 1680 against 1715 us per backward call).
+int bwd_hsplit(int B, int H, int H_kv, int N, int d) {
   const int group = H / H_kv;
   const int n_kblk = (N + fa::kBwdKvRows - 1) / fa::kBwdKvRows;
   const int64_t wgs = (int64_t)n_kblk * B * H_kv;
-  int want = (int)std::min<int64_t>(group, (1024 + wgs - 1) / wgs);
+  const int64_t target = d == 128 ? 512 : 1024;
+  int want = (int)std::min<int64_t>(group, (target + wgs - 1) / wgs);
   while (group % want) want--;
   return std::max(want, 1);
 }
@@ -437,7 +441,7 @@ size_t bwd_dsum_bytes(int B, int H, int N) {
   return ((size_t)B * H * N * sizeof(float) + 255) / 256 * 256;
 }
 size_t bwd_ws_bytes(int B, int H, int H_kv, int N, int d) {
-  const int hs = bwd_hsplit(B, H, H_kv, N);
+  const int hs = bwd_hsplit(B, H, H_kv, N, d);
   return bwd_dsum_bytes(B, H, N) + (hs > 1 ? 2 * (size_t)hs * B * H_kv * N * d * sizeof(float) : 0);
 }
 
@@ -517,7 +521,7 @@ int fa_bwd(const void* q, const void* k, const void* v, const void* o, const voi
   a.dk = static_cast<fa::bf16*>(dk);
   a.dv = static_cast<fa::bf16*>(dv);
   a.dsum = static_cast<float*>(workspace);
-  a.hsplit = bwd_hsplit(B, H, H_kv, N);
+  a.hsplit = bwd_hsplit(B, H, H_kv, N, d);
   a.part = reinterpret_cast<float*>(static_cast<char*>(workspace) + bwd_dsum_bytes(B, H, N));
   a.N = N;
   a.H = H;

@@ -294,9 +294,11 @@ def test_backward_workspace_bytes():
     f = fa.fa_bwd_workspace_bytes
     # D (B*H*N floats, 256-byte aligned) only, when no query-head split is needed (MHA)
     assert f(2, 8, 8, 300, 128) == 2 * 8 * 300 * 4
-    # Llama-3-8B grouped layer: 32 key blocks x 8 K/V heads = 256 workgroups -> 4 splits, each
-    # with fp32 partial dK and dV
-    assert f(1, 32, 8, 8192, 128) == 32 * 8192 * 4 + 2 * 4 * 8 * 8192 * 128 * 4
+    # Llama-3-8B grouped layer: 32 key blocks x 8 K/V heads = 256 workgroups -> 2 splits at
+    # d = 128 (about two workgroups per CU), 4 at d = 64 (about four), each with fp32 partial dK
+    # and dV
+    assert f(1, 32, 8, 8192, 128) == 32 * 8192 * 4 + 2 * 2 * 8 * 8192 * 128 * 4
+    assert f(1, 32, 8, 8192, 64) == 32 * 8192 * 4 + 2 * 4 * 8 * 8192 * 64 * 4
     # few workgroups: the split is the largest divisor of the group size up to the need
     assert f(2, 8, 2, 300, 128) == 19200 + 2 * 4 * 2 * 2 * 300 * 128 * 4
     assert f(0, 8, 8, 300, 128) == 0
