@@ -196,20 +196,27 @@ __global__ __launch_bounds__(kExtWaves * 64) __attribute__((amdgpu_waves_per_eu(
   const char* kh = reinterpret_cast<const char*>(a.k + kvhead);
   const char* vh = reinterpret_cast<const char*>(a.v + kvhead);
   const int t_first = blo / TK, t_last = bhi / TK;  // tiles with a key some row of the block sees
+  // Causal ALiBi (without a bias) walks the tiles from the diagonal down: its term grows by
+  // slope * 32 per step towards the diagonal, so in key order the row maximum, hence the lazy
+  // reference, would move (and the accumulator be rescaled) on nearly every step of the heads with
+  // large slopes; from the diagonal down it is set by the first steps and rarely moves again.
+  constexpr bool DESC = CAUSAL && ALIBI && !BIAS;
   if (t_first <= t_last) {
-    dma_tile<D, TK, kExtWaves>(sK2[0], kh, rs, t_first * TK, N, wave, lane);
-    dma_tile<D, TK, kExtWaves>(sV2[0], vh, rs, t_first * TK, N, wave, lane);
+    dma_tile<D, TK, kExtWaves>(sK2[0], kh, rs, (DESC ? t_last : t_first) * TK, N, wave, lane);
+    dma_tile<D, TK, kExtWaves>(sV2[0], vh, rs, (DESC ? t_last : t_first) * TK, N, wave, lane);
     if constexpr (BIAS) dma_bias(sB2[0], t_first * TK);
     wait_dma();
     __syncthreads();
   }
-  // Tile t sits in stage (t - t_first) % 2; the stage is a compile-time constant of each copy of
-  // the loop body, so every LDS address is a per-lane offset plus an immediate.
+  // Tile t sits in stage (t - t_first) % 2 (DESC: (t_last - t) % 2); the stage is a compile-time
+  // constant of each copy of the loop body, so every LDS address is a per-lane offset plus an
+  // immediate.
   auto tile = [&](auto stage_c, int t) {
     constexpr int st = decltype(stage_c)::value;
-    if (t < t_last) {
-      dma_tile<D, TK, kExtWaves>(sK2[st ^ 1], kh, rs, (t + 1) * TK, N, wave, lane);
-      dma_tile<D, TK, kExtWaves>(sV2[st ^ 1], vh, rs, (t + 1) * TK, N, wave, lane);
+    const bool more = DESC ? t > t_first : t < t_last;  // a next tile: t - 1 (DESC) or t + 1
+    if (more) {
+      dma_tile<D, TK, kExtWaves>(sK2[st ^ 1], kh, rs, (DESC ? t - 1 : t + 1) * TK, N, wave, lane);
+      dma_tile<D, TK, kExtWaves>(sV2[st ^ 1], vh, rs, (DESC ? t - 1 : t + 1) * TK, N, wave, lane);
     }
     // bias tile of K/V tiles t.. (if t starts one): stage bst; its first tile requests the next
     // bias tile into the other stage, after K/V so that the wait below can leave it in flight
@@ -228,7 +235,8 @@ __global__ __launch_bounds__(kExtWaves * 64) __attribute__((amdgpu_waves_per_eu(
     const char* sB = sB2[bst];
     constexpr int bkey0 = TPB == 1 ? 0 : st * TK;  // this tile's first key within the bias tile
 #pragma unroll
-    for (int sb = 0; sb < TK / 32; sb++) {
+    for (int sbi = 0; sbi < TK / 32; sbi++) {
+      const int sb = DESC ? TK / 32 - 1 - sbi : sbi;  // 32-key steps of the tile, in tile order
       const int k0 = t * TK + 32 * sb;
       // wave-uniform: no key of this step is visible to any row of the wave
       if (wq0 >= N || k0 > whi || k0 + 31 < wlo) continue;  // (continue: next sb)
@@ -324,7 +332,7 @@ __global__ __launch_bounds__(kExtWaves * 64) __attribute__((amdgpu_waves_per_eu(
           acc[db] = __builtin_amdgcn_mfma_f32_32x32x16_bf16(tile_tr_at<D>(sV, lo_, 32 * sb + 16 * ks, db),
                                                             pf[ks], acc[db], 0, 0, 0);
     }
-    if (t < t_last) {
+    if (more) {
       // K/V of tile t + 1 are the oldest loads in flight; a bias tile requested in this tile may
       // stay in flight until the end of the next one (TPB = 2), by which its first tile is due
       if (TPB == 2 && bias_issued)
@@ -334,9 +342,16 @@ __global__ __launch_bounds__(kExtWaves * 64) __attribute__((amdgpu_waves_per_eu(
       __syncthreads();
     }
   };
-  for (int t = t_first; t <= t_last; t += 2) {
-    tile(std::integral_constant<int, 0>{}, t);
-    if (t + 1 <= t_last) tile(std::integral_constant<int, 1>{}, t + 1);
+  if constexpr (DESC) {
+    for (int t = t_last; t >= t_first; t -= 2) {
+      tile(std::integral_constant<int, 0>{}, t);
+      if (t - 1 >= t_first) tile(std::integral_constant<int, 1>{}, t - 1);
+    }
+  } else {
+    for (int t = t_first; t <= t_last; t += 2) {
+      tile(std::integral_constant<int, 0>{}, t);
+      if (t + 1 <= t_last) tile(std::integral_constant<int, 1>{}, t + 1);
+    }
   }
 
   const float lt = half_swap_sum(l);
