@@ -16,9 +16,10 @@
 //     S^T = K Q^T, dP^T = V dO^T (keys on M, queries on N, as in the forward kernel), P^T and dS^T
 //     in fp32, then dQ^T += K^T dS^T with dS^T rounded to bf16 as the B operand and K^T read
 //     with the transposing LDS read.
-//   fa_bwd_dkdv_kernel (keys outermost; d = 64 -- at d = 128 its wide form in fa_bwd_wide.h, with
-//     the same arithmetic in the same order): 8 waves x 32 keys per workgroup (two per SIMD). A wave keeps its keys'
-//     K and V rows in registers as B operands and loops over the query tiles -- of every query
+//   fa_bwd_dkdv_kernel (keys outermost; d = 64 -- at d = 128 its wide form in fa_bwd_wide.h,
+//     with the same arithmetic in the same order): 8 waves x 32 keys per workgroup (two per
+//     SIMD). A wave keeps its keys' K rows in registers and their V rows in LDS as B operands
+//     and loops over the query tiles -- of every query
 //     head that shares the K/V head, so grouped heads receive the sum of their query heads'
 //     gradients -- with Q, dO, L and D of each 64-query tile in LDS: S = Q K^T, dP = dO V^T
 //     (queries on M, keys on N), P and dS in fp32, then dV^T += dO^T P and dK^T += Q^T dS with

@@ -154,8 +154,9 @@ int fa_fwd_ext(const void* q, const void* k, const void* v, void* o, float* lse,
  *   16-byte aligned, overlapping nothing else; its contents on entry do not matter and are
  *   overwritten). Two kernels are enqueued on `stream`; calls that share a workspace must not
  *   overlap. Limits: N_kv <= 2^22, (H / H_kv) * N_q <= 512 (the query rows that share one K/V
- *   head, stacked and cut into 32-row tiles; more return FA_ERR_UNSUPPORTED), d in {64, 128}. Other conventions and
- *   return codes as fa_fwd_gqa; a workspace that is NULL or too small returns FA_ERR_INVALID_ARG.
+ *   head, stacked and cut into 32-row tiles; more return FA_ERR_UNSUPPORTED), d in {64, 128}.
+ *   Other conventions and return codes as fa_fwd_gqa; a workspace that is NULL or too small
+ *   returns FA_ERR_INVALID_ARG.
  */
 size_t fa_splitkv_workspace_bytes(int B, int H, int H_kv, int N_q, int N_kv, int d, int causal,
                                   int n_splits);
