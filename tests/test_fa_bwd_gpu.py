@@ -130,6 +130,22 @@ def test_backward_ragged_shapes(N, H, H_kv, d, causal, layout):
     check(got, ref, bnd, "N=%d" % N)
 
 
+@pytest.mark.parametrize("N,H,H_kv,causal,layout", [(513, 2, 2, False, "bhnd"),
+                                                   (1000, 4, 2, True, "bnhd"),
+                                                   (777, 4, 1, True, "bnhd"),
+                                                   (1300, 2, 2, True, "bhnd")])
+def test_backward_several_key_blocks(N, H, H_kv, causal, layout):
+    # d = 128 over several 256-key blocks of the dK/dV kernel (one wave per 64 keys): ragged last
+    # blocks, waves whose keys all lie past N, grouped heads split over workgroups, both layouts.
+    log("bwd several key blocks N=%d H=%d H_kv=%d causal=%s %s" % (N, H, H_kv, causal, layout))
+    q, k, v = make_inputs(1, H, N, 128, H_kv=H_kv, seed=N + 5)
+    do = make_inputs(1, H, N, 128, seed=N + 6)[0]
+    scale = softmax_scale(128)
+    got = gpu_fwd_bwd(q, k, v, do, scale, causal, layout)
+    ref, bnd = reference(q, k, v, do, scale, causal)
+    check(got, ref, bnd, "N=%d" % N)
+
+
 def test_backward_large_scores():
     # Scaled-up queries and enlarged keys: P is nearly one-hot in many rows.
     q, k, v = make_inputs(1, 4, 1024, 128, seed=31, q_mult=8.0, outlier_frac=0.01, outlier_mult=4.0)
