@@ -1,5 +1,6 @@
-// Wide-row forward kernel for gfx950, head dim 128: the bench workload (causal Llama-3-8B layer)
-// and the other large d = 128 grids (the choice is made in fa_api.hip).
+// Wide-row forward kernel for gfx950, head dim 128: the bench workload (causal Llama-3-8B layer),
+// the other large d = 128 grids, and causal sliding windows on them (the choice is made in
+// fa_api.hip).
 //
 // The method is the one of the other forward kernels ("FlashAttention-2 -- Deeper Math", Fixes
 // 1-5 and "Causal masking: skip the blocks"; "Understanding FlashAttention Pt 1", §2.4 and §3.1):
@@ -38,6 +39,9 @@
 //     tile t (V of its second step, P4 of its first step) precedes it and the first reads of tile
 //     t+1 (K of the next step, P2; V of the next step, P4) follow it. The DMA pieces of tile t+2
 //     are issued one per MFMA group of that P2. The epilogue stores O through LDS as whole rows.
+//   * With a causal sliding window (row q sees keys q - wl .. q) a workgroup starts at the tile of
+//     its first row's first key; the steps before a block's window are masked like those past its
+//     diagonal (the waves above the first row run through a few fully masked steps first).
 //   * Every wave takes part in every tile of its workgroup's key range, so the barrier counts
 //     match. The steps past a block's causal diagonal (or past N) are fully masked, which makes
 //     their probabilities 0 and leaves the running state unchanged; once a whole tile is past both
@@ -53,6 +57,7 @@ constexpr int kWideRows = 64 * kWideWaves;  // query rows per workgroup
 constexpr int kWideSlack = 2;               // lazy reference: moved when exceeded by > 2 (log2)
 constexpr int kWideTK = 64;                 // keys per LDS tile (two 32-key steps)
 constexpr int kWideStages = 2;              // LDS stages of the K/V tile ring
+constexpr int kWideNoWindow = 1 << 30;      // WideArgs::wl when there is no sliding window
 
 struct WideArgs {
   const bf16* q;
@@ -60,6 +65,7 @@ struct WideArgs {
   const bf16* v;
   bf16* o;
   float* lse;
+  int wl;  // causal sliding window (the window instantiation): row q sees keys q - wl .. q
   int N, H, group, BH, n_qblk;
   float scale_log2;
   long long q_bs, q_hs, kv_bs, kv_hs;
@@ -89,12 +95,16 @@ __device__ __forceinline__ float wide_max16(const f32x16& v) {
 }
 
 // For a step whose keys (from k0) may pass the last key `last_key` of the lane's row (the causal
-// diagonal, the end of the sequence, the padding steps past both): those keys become -inf, and the
-// maximum is taken again. Rare; wave-uniform branch.
-__device__ __forceinline__ void wide_mask(WideBlock& x, int k0, int last_key, int h) {
+// diagonal, the end of the sequence, the padding steps past both) or, with a sliding window, lie
+// before its first key: those keys become -inf, and the maximum is taken again. Rare; wave-uniform
+// branch.
+template <bool WINDOW>
+__device__ __forceinline__ void wide_mask(WideBlock& x, int k0, int last_key, int first_key, int h) {
   const int hi = last_key - k0 - 4 * h;
+  const int lo = first_key - k0 - 4 * h;  // (window) keys before first_key are hidden as well
 #pragma unroll
-  for (int i = 0; i < 16; i++) x.x[i] = acc_row(i, 0) <= hi ? x.x[i] : -INFINITY;
+  for (int i = 0; i < 16; i++)
+    x.x[i] = acc_row(i, 0) <= hi && (!WINDOW || acc_row(i, 0) >= lo) ? x.x[i] : -INFINITY;
   x.xmax = wide_max16(x.x);
 }
 
@@ -261,8 +271,9 @@ struct WideDma {
   }
 };
 
-template <bool CAUSAL>
+template <bool CAUSAL, bool WINDOW>
 __global__ __launch_bounds__(kWideWaves * 64) __attribute__((amdgpu_waves_per_eu(1, 1))) void fa_fwd_wide_kernel(WideArgs a) {
+  static_assert(CAUSAL || !WINDOW, "the sliding window is the causal one (keys q - wl .. q)");
   constexpr int D = 128, DK = 8, DB = 4, TK = kWideTK, SPT = TK / 32;  // steps per tile
   using S = Swz<D>;
   constexpr int TILE = S::template bytes<TK>();
@@ -306,6 +317,12 @@ __global__ __launch_bounds__(kWideWaves * 64) __attribute__((amdgpu_waves_per_eu
   // first row needs a mask (wave-uniform). Once a block needs one, every later step of it does.
   const int lastA = min(N - 1, CAUSAL ? ra + c : N - 1), lastB = min(N - 1, CAUSAL ? rb + c : N - 1);
   const int edgeA = min(N - 1, CAUSAL ? ra : N - 1), edgeB = min(N - 1, CAUSAL ? rb : N - 1);
+  // Sliding window: the first key of each lane's row, and the last first key of each block (a step
+  // starting before it needs the lower mask). The workgroup starts at the tile of its first row's
+  // first key; the waves above it run through a few fully masked steps first.
+  const int wl = WINDOW ? a.wl : 0;
+  const int firstA = ra + c - wl, firstB = rb + c - wl;
+  const int ledgeA = ra + 31 - wl, ledgeB = rb + 31 - wl;
 
   LaneOffsets<D> lo_;
   lo_.init(lane);
@@ -314,6 +331,7 @@ __global__ __launch_bounds__(kWideWaves * 64) __attribute__((amdgpu_waves_per_eu
   const char* kh = reinterpret_cast<const char*>(a.k + kvhead);
   const char* vh = reinterpret_cast<const char*>(a.v + kvhead);
   const int n_tiles = (CAUSAL ? bq1 : N - 1) / TK + 1;
+  const int t_lo = WINDOW ? max(0, bq0 - wl) / TK : 0;  // first tile
   // buffer resources over rows t TK .. min(N, (t + 1) TK) - 1 of K and V (bytes past read as 0;
   // none for tiles past N, whose loads then only write zeros to a stage nothing reads again)
   auto tile_rsrc2 = [&](int t, i32x4v& rk, i32x4v& rv) __attribute__((always_inline)) {
@@ -346,10 +364,10 @@ __global__ __launch_bounds__(kWideWaves * 64) __attribute__((amdgpu_waves_per_eu
     for (int dk = 0; dk < DK; dk++) kf[dk] = tile_row_at<D>(tile, lo_, r, dk);
   };
 
-  // prologue: tiles 0 and 1 requested, tile 0 awaited; S_A(0) shifted and checked
-  issue_tile(0, 0);
-  if (n_tiles > 1) {
-    issue_tile(1, 1);
+  // prologue: tiles t_lo and t_lo + 1 requested, tile t_lo awaited; S_A(0) shifted and checked
+  issue_tile(t_lo, 0);
+  if (t_lo + 1 < n_tiles) {
+    issue_tile(t_lo + 1, 1);
     wait_dma_but<2 * WideDma<TK, NS>::PW>();
   } else {
     wait_dma();
@@ -367,7 +385,8 @@ __global__ __launch_bounds__(kWideWaves * 64) __attribute__((amdgpu_waves_per_eu
     for (int i = 0; i < 16; i++) A.x[i] = __builtin_fmaf(s0[i], sl2, -A.ref);
     A.xmax = wide_max16(A.x);
   }
-  if (31 > edgeA) wide_mask(A, 0, lastA, h);
+  if (t_lo * TK + 31 > edgeA || (WINDOW && t_lo * TK < ledgeA))
+    wide_mask<WINDOW>(A, t_lo * TK, lastA, firstA, h);
   wide_check(A);
 
   // Step j (sub-step sb of tile t, in stage st): the four phases of the header comment.
@@ -402,7 +421,8 @@ __global__ __launch_bounds__(kWideWaves * 64) __attribute__((amdgpu_waves_per_eu
       }
     });
     if constexpr (LAST) race_check_drain();
-    if (__builtin_expect(k0 + 31 > edgeB, 0)) wide_mask(B, k0, lastB, h);
+    if (__builtin_expect(k0 + 31 > edgeB || (WINDOW && k0 < ledgeB), 0))
+      wide_mask<WINDOW>(B, k0, lastB, firstB, h);
     wide_check(B);
     // P3: S_A(j+1) = K(j+1) Q_A^T; probabilities of B, step j
     phase_exp(A, kf, B, [](int) {});
@@ -414,7 +434,8 @@ __global__ __launch_bounds__(kWideWaves * 64) __attribute__((amdgpu_waves_per_eu
       vnext[i & 3][i >> 2] = LAST ? tile_tr_at<D>(sV[st ^ 1], lo_, 16 * (i >> 2), i & 3)
                                   : tile_tr_at<D>(sV[st], lo_, 32 * (sb + 1) + 16 * (i >> 2), i & 3);
     });
-    if (__builtin_expect(k0 + 63 > edgeA, 0)) wide_mask(A, k0 + 32, lastA, h);
+    if (__builtin_expect(k0 + 63 > edgeA || (WINDOW && k0 + 32 < ledgeA), 0))
+      wide_mask<WINDOW>(A, k0 + 32, lastA, firstA, h);
     wide_check(A);
   };
   auto run_tile = [&](auto st_c, int tt) __attribute__((always_inline)) {
@@ -443,7 +464,7 @@ __global__ __launch_bounds__(kWideWaves * 64) __attribute__((amdgpu_waves_per_eu
     for (int i = 0; i < WideDma<TK, NS>::PW; i++) dma.piece(st, 1, i, rv);
     race_check_drain();
   };
-  int t = 0;
+  int t = t_lo;  // tile t sits in stage (t - t_lo) % 2
   for (; t + 1 < n_real; t += 2) {
     run_tile(std::integral_constant<int, 0>{}, t);
     run_tile(std::integral_constant<int, 1>{}, t + 1);
@@ -453,7 +474,7 @@ __global__ __launch_bounds__(kWideWaves * 64) __attribute__((amdgpu_waves_per_eu
     t++;
   }
   for (; t < n_tiles; t++) {
-    if (t & 1) idle_tile(std::integral_constant<int, 1>{}, t);
+    if ((t - t_lo) & 1) idle_tile(std::integral_constant<int, 1>{}, t);
     else idle_tile(std::integral_constant<int, 0>{}, t);
   }
 

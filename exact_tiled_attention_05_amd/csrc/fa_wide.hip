@@ -13,8 +13,10 @@ __attribute__((visibility("hidden"))) hipError_t launch_wide(const WideArgs& arg
                                                            hipStream_t stream) {
   WideArgs a = args;
   void* argv[] = {&a};
-  const void* fn = causal ? reinterpret_cast<const void*>(&fa_fwd_wide_kernel<true>)
-                          : reinterpret_cast<const void*>(&fa_fwd_wide_kernel<false>);
+  const bool window = causal && a.wl < kWideNoWindow;
+  const void* fn = window ? reinterpret_cast<const void*>(&fa_fwd_wide_kernel<true, true>)
+                 : causal ? reinterpret_cast<const void*>(&fa_fwd_wide_kernel<true, false>)
+                          : reinterpret_cast<const void*>(&fa_fwd_wide_kernel<false, false>);
   return hipLaunchKernel(fn, dim3(a.n_qblk * a.BH), dim3(kWideWaves * 64), argv, 0, stream);
 }
 

@@ -103,6 +103,21 @@ def test_alibi(N, d, causal, window):
     check(q, k, v, softmax_scale(d), causal, "bnhd", window, alibi(H), tag="alibi")
 
 
+@pytest.mark.parametrize("B,N,H,H_kv,layout,window", [
+    (1, 4096, 4, 4, "bhnd", (4095, -1)), (2, 4097, 4, 2, "bnhd", (1000, 7)),
+    (1, 5000, 2, 1, "bnhd", (63, -1)), (1, 4160, 2, 2, "bhnd", (0, -1)),
+    (1, 4500, 2, 2, "bnhd", (300, 0)), (1, 4096, 2, 2, "bhnd", (10000, -1))])
+def test_window_long_causal(B, N, H, H_kv, layout, window):
+    """A causal sliding window at d = 128 and N >= 4096 (on the wide-row kernel): windows of one
+    key, of less and more than a workgroup's rows, and wider than N, with and without a right bound
+    (which the causal rule makes moot); ragged lengths, grouped heads, both layouts; sampled rows
+    plus the first and last 70 rows."""
+    q, k, v = make_inputs(B, H, N, 128, H_kv=H_kv, seed=N + window[0])
+    rows = np.unique(np.concatenate([sampled_rows(N, 96, seed=N + 1).numpy(),
+                                     np.arange(0, 70), np.arange(N - 70, N)]))
+    check(q, k, v, softmax_scale(128), True, layout, window, rows=rows, tag="window long causal")
+
+
 @pytest.mark.parametrize("B,N,H,H_kv,layout,slope_mult,scale_mult", [
     (1, 4096, 4, 4, "bhnd", 1.0, 1.0), (2, 4097, 4, 2, "bnhd", 1.0, 1.0),
     (1, 5000, 2, 1, "bnhd", 64.0, 1.0), (1, 4160, 2, 2, "bhnd", 0.25, 0.05)])
