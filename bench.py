@@ -409,7 +409,7 @@ def bench_variant(args, w):
         "config": {"workload": args.workload, "B": B, "H": H, "H_kv": H_kv, "N": N, "d": d,
                    "causal": causal, "layout": layout, "window": list(window),
                    "alibi": bool(w.get("alibi")), "bias": bias is not None,
-                   "kernel": "fa_fwd_ext (fa_fwd_ext_kernel)"},
+                   "kernel": "fa_fwd_ext (%s)" % device_kernel(args.workload)},
         "roofline": {"bound": "mfma", "achieved": round(tflops, 2), "peak": PEAK_BF16_TFLOPS,
                      "unit": "TFLOP/s", "frac": round(tflops / PEAK_BF16_TFLOPS, 4),
                      "traffic": recorded_traffic(args.workload)},
@@ -539,12 +539,16 @@ def workload_family(workload):
         return "decode"
     if w.get("backward"):
         return "bwd"
-    # fa_api.hip: every variant runs the 4-wave kernel; plain bf16 d = 128 with N >= 4096 the
-    # wide-row kernel; d = 256, the rest of causal d = 128 and grids of more than 2^16 query rows
-    # the 4-wave kernel; the remaining small grids the 8-wave kernel
-    if w.get("window") or w.get("alibi") or w.get("bias_seed"):
+    # fa_api.hip: bf16 d = 128 with N >= 4096 runs the wide-row kernel, plain or with a causal
+    # sliding window; every other variant (ALiBi, bias, other windows) runs the 4-wave kernel, and
+    # so do d = 256, the rest of causal d = 128 and grids of more than 2^16 query rows; the
+    # remaining small grids run the 8-wave kernel
+    long128 = w["dtype"] == "bf16" and w["d"] == 128 and w["N"] >= 4096
+    if w.get("alibi") or w.get("bias_seed"):
         return "ext"
-    if w["dtype"] == "bf16" and w["d"] == 128 and w["N"] >= 4096:
+    if w.get("window"):
+        return "wide" if long128 and w["causal"][-1] and w["window"][0] >= 0 else "ext"
+    if long128:
         return "wide"
     if (w["d"] == 256 or (w["dtype"] == "bf16" and ((w["d"] == 128 and w["causal"][-1])
                                                     or w["B"] * w["H"] * w["N"] > (1 << 16)))):
