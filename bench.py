@@ -539,13 +539,15 @@ def workload_family(workload):
         return "decode"
     if w.get("backward"):
         return "bwd"
-    # fa_api.hip: bf16 d = 128 with N >= 4096 runs the wide-row kernel, plain or with a causal
-    # sliding window; every other variant (ALiBi, bias, other windows) runs the 4-wave kernel, and
-    # so do d = 256, the rest of causal d = 128 and grids of more than 2^16 query rows; the
-    # remaining small grids run the 8-wave kernel
+    # fa_api.hip: bf16 d = 128 with N >= 4096 runs the wide-row kernel, plain, with a causal
+    # sliding window or with causal ALiBi (alone); every other variant (bias, other windows, other
+    # ALiBi) runs the 4-wave kernel, and so do d = 256, the rest of causal d = 128 and grids of
+    # more than 2^16 query rows; the remaining small grids run the 8-wave kernel
     long128 = w["dtype"] == "bf16" and w["d"] == 128 and w["N"] >= 4096
-    if w.get("alibi") or w.get("bias_seed"):
+    if w.get("bias_seed"):
         return "ext"
+    if w.get("alibi"):
+        return "wide" if long128 and w["causal"][-1] and not w.get("window") else "ext"
     if w.get("window"):
         return "wide" if long128 and w["causal"][-1] and w["window"][0] >= 0 else "ext"
     if long128:

@@ -120,7 +120,8 @@ hipError_t launch_ext_d(fa::ExtArgs a, int causal, hipStream_t s) {
 }
 
 int run_wide(const void* q, const void* k, const void* v, void* o, float* lse, int B, int H,
-             int H_kv, int N, float scale, int causal, int layout, int window_left, void* stream);
+             int H_kv, int N, float scale, int causal, int layout, int window_left,
+             const float* slopes, void* stream);
 
 int run_ext(const void* q, const void* k, const void* v, void* o, float* lse, int B, int H,
             int H_kv, int N, int d, float scale, int causal, int layout, int window_left,
@@ -134,13 +135,19 @@ int run_ext(const void* q, const void* k, const void* v, void* o, float* lse, in
   // key tile and masks keys before a row's window. Grouped Llama layer with a 4095-key window
   // (one box, alternating runs): see the measurement notes.
   if (causal && !slopes && !bias && d == 128 && N >= 4096 && window_left >= 0)
-    return run_wide(q, k, v, o, lse, B, H, H_kv, N, scale, causal, layout, window_left, stream);
+    return run_wide(q, k, v, o, lse, B, H, H_kv, N, scale, causal, layout, window_left, nullptr,
+                    stream);
   const size_t qb = (size_t)B * H * N * d * 2, lb = (size_t)B * H * N * sizeof(float);
   if (slopes) {
     if (reinterpret_cast<uintptr_t>(slopes) & 3) return FA_ERR_ALIGNMENT;
     if (ranges_overlap(slopes, H * sizeof(float), o, qb) ||
         ranges_overlap(slopes, H * sizeof(float), lse, lb))
       return FA_ERR_INVALID_ARG;
+    // Causal ALiBi alone at d = 128 and N >= 4096: the wide-row kernel, which walks the key tiles
+    // from the diagonal down for it (its ALiBi term divides by the scale: scales below 1e-6 stay
+    // on the 4-wave kernel).
+    if (causal && !bias && d == 128 && N >= 4096 && window_left < 0 && scale >= 1e-6f)
+      return run_wide(q, k, v, o, lse, B, H, H_kv, N, scale, causal, layout, -1, slopes, stream);
   }
   if (bias) {
     if (bias_bs < 0 || bias_hs < 0 || bias_rs < N) return FA_ERR_INVALID_ARG;
@@ -191,11 +198,13 @@ int run_ext(const void* q, const void* k, const void* v, void* o, float* lse, in
 }
 
 int run_wide(const void* q, const void* k, const void* v, void* o, float* lse, int B, int H,
-             int H_kv, int N, float scale, int causal, int layout, int window_left, void* stream) {
+             int H_kv, int N, float scale, int causal, int layout, int window_left,
+             const float* slopes, void* stream) {
   const int rc = check_args(q, k, v, o, lse, B, H, H_kv, N, 128, scale, causal, layout, 2);
   if (rc != FA_OK) return rc;
   fa::WideArgs a;
   a.wl = window_left < 0 ? fa::kWideNoWindow : std::min(window_left, N);
+  a.slopes = slopes;
   a.q = static_cast<const fa::bf16*>(q);
   a.k = static_cast<const fa::bf16*>(k);
   a.v = static_cast<const fa::bf16*>(v);
@@ -217,7 +226,7 @@ int run_bf16(const void* q, const void* k, const void* v, void* o, float* lse, i
   // N=4096 1166 / 1070. Below N = 4096 its 256-row workgroups leave too few (and, causal, too
   // unequal) blocks: causal N=2048 561 / 628, N=1024 251 / 322.
   if (d == 128 && N >= 4096)
-    return run_wide(q, k, v, o, lse, B, H, H_kv, N, scale, causal, layout, -1, stream);
+    return run_wide(q, k, v, o, lse, B, H, H_kv, N, scale, causal, layout, -1, nullptr, stream);
   // Which forward kernel: the 4-wave kernel of the variants (no variant enabled) for d = 256, for
   // causal d = 128 and for every grid of more than 2^16 query rows; the 8-wave kernel for the
   // remaining small grids. Measured on one box (alternating runs): the 4-wave kernel is 2.7-4.2%

@@ -65,6 +65,7 @@ struct WideArgs {
   const bf16* v;
   bf16* o;
   float* lse;
+  const float* slopes;  // ALiBi slopes, one per query head (the ALiBi instantiation)
   int wl;  // causal sliding window (the window instantiation): row q sees keys q - wl .. q
   int N, H, group, BH, n_qblk;
   float scale_log2;
@@ -128,6 +129,14 @@ __device__ __forceinline__ void wide_fix(WideBlock& x) {
   for (int i = 0; i < 16; i++) x.x[i] -= delta;
 }
 
+// The step after a block's last one, when the keys run from the diagonal down (its keys would be
+// negative): every score hidden.
+__device__ __forceinline__ void wide_mask_all(WideBlock& x) {
+#pragma unroll
+  for (int i = 0; i < 16; i++) x.x[i] = -INFINITY;
+  x.xmax = -INFINITY;
+}
+
 __device__ __forceinline__ void wide_check(WideBlock& x) {
   if (__builtin_expect(__any(x.xmax > x.thr), 0)) wide_fix(x);
 }
@@ -140,10 +149,12 @@ __device__ __forceinline__ void wide_check(WideBlock& x) {
 // Exponential phase: S_Y = K Q_Y^T (a chain of 8 MFMAs) with the probabilities of block X: per
 // group two exponentials, and the bf16 packing and pair sum of the previous group's two. load(i)
 // issues the LDS reads that belong to group i.
-template <class Load>
+template <bool ALIBI, class Load>
 __device__ __forceinline__ void phase_exp(WideBlock& Y, const bf16x8 (&kf)[8], WideBlock& X,
-                                          Load&& load) {
-  f32x16 s = f32x16{};
+                                          const f32x16& s_init, Load&& load) {
+  f32x16 s;
+  if constexpr (ALIBI) s = s_init;  // the per-register part of the ALiBi term, over the scale
+  else s = f32x16{};
   float e[16];
 #pragma unroll
   for (int i = 0; i < 8; i++) {
@@ -175,12 +186,17 @@ __device__ __forceinline__ void phase_exp(WideBlock& Y, const bf16x8 (&kf)[8], W
 // Shift phase: O_X += V^T P_X^T (8 MFMAs on 4 accumulators) with X's row-sum update and block Y's
 // scores moved to log2 units relative to its reference, x = s scale log2(e) - ref, and their
 // maximum (the rare reference move and the masks follow the phase).
-template <class Load>
+template <bool ALIBI, class Load>
 __device__ __forceinline__ void phase_pv(WideBlock& X, const bf16x8 (&vf)[4][2], WideBlock& Y,
-                                         float scale_log2, Load&& load) {
+                                         float scale_log2, float yadd, Load&& load) {
   float m1 = 0.f, m2 = 0.f, m3 = 0.f;
   float* t = X.t;
-  auto sh = [&](int i) { Y.x[i] = __builtin_fmaf(Y.x[i], scale_log2, -Y.ref); pin(Y.x[i]); };
+  // ALiBi: yadd = the step's part of the ALiBi term minus the reference
+  auto sh = [&](int i) {
+    if constexpr (ALIBI) Y.x[i] = __builtin_fmaf(Y.x[i], scale_log2, yadd);
+    else Y.x[i] = __builtin_fmaf(Y.x[i], scale_log2, -Y.ref);
+    pin(Y.x[i]);
+  };
 #pragma unroll
   for (int i = 0; i < 8; i++) {
     const int ks = i >> 2, db = i & 3;
@@ -271,9 +287,12 @@ struct WideDma {
   }
 };
 
-template <bool CAUSAL, bool WINDOW>
+template <bool CAUSAL, bool WINDOW, bool ALIBI>
 __global__ __launch_bounds__(kWideWaves * 64) __attribute__((amdgpu_waves_per_eu(1, 1))) void fa_fwd_wide_kernel(WideArgs a) {
   static_assert(CAUSAL || !WINDOW, "the sliding window is the causal one (keys q - wl .. q)");
+  static_assert(!ALIBI || (CAUSAL && !WINDOW), "ALiBi: causal, without a window");
+  // ALiBi walks the key tiles from the diagonal down (see the ALiBi note below)
+  constexpr bool DESC = ALIBI;
   constexpr int D = 128, DK = 8, DB = 4, TK = kWideTK, SPT = TK / 32;  // steps per tile
   using S = Swz<D>;
   constexpr int TILE = S::template bytes<TK>();
@@ -313,8 +332,29 @@ __global__ __launch_bounds__(kWideWaves * 64) __attribute__((amdgpu_waves_per_eu
   A.ref = B.ref = 0.f;
 
   A.l = B.l = 0.f;
+  // ALiBi (causal): the score of row r0 + c (block from r0) and key k0 + acc_row(i, h) (register
+  // i of a step from k0) gains -slope (q - k) = slope (k0 - r0) - slope c + slope acc_row(i, h).
+  // The last part depends only on the register: it seeds the score MFMAs' accumulator, divided by
+  // the scale (aini); the rest is added with the reference once per step, in log2 units
+  // u = slope log2(e) (k0 - r0) + alane, every term small near the diagonal. The term grows by
+  // 32 slope log2(e) per step towards the diagonal, so in key order the row maximum, and with it
+  // the lazy reference, would move on nearly every step of the heads with large slopes; the keys
+  // are walked from the diagonal down instead, where the first steps set the reference.
+  f32x16 aini = f32x16{};
+  float slope2 = 0.f, alane = 0.f;
+  if constexpr (ALIBI) {
+    slope2 = a.slopes[hq] * kLog2e;
+    const float per_key = slope2 / sl2;
+#pragma unroll
+    for (int i = 0; i < 16; i++) aini[i] = per_key * (float)acc_row(i, h);
+    alane = -slope2 * (float)c;
+  }
+  auto yadd = [&](const WideBlock& x, int k0, int r0) __attribute__((always_inline)) {
+    return ALIBI ? __builtin_fmaf(slope2, (float)(k0 - r0), alane) - x.ref : 0.f;
+  };
   // The last key each lane's row sees; a step whose last key passes the last key of its block's
-  // first row needs a mask (wave-uniform). Once a block needs one, every later step of it does.
+  // first row needs a mask (wave-uniform): in key order the block's last steps, from the diagonal
+  // down its first ones.
   const int lastA = min(N - 1, CAUSAL ? ra + c : N - 1), lastB = min(N - 1, CAUSAL ? rb + c : N - 1);
   const int edgeA = min(N - 1, CAUSAL ? ra : N - 1), edgeB = min(N - 1, CAUSAL ? rb : N - 1);
   // Sliding window: the first key of each lane's row, and the last first key of each block (a step
@@ -335,8 +375,9 @@ __global__ __launch_bounds__(kWideWaves * 64) __attribute__((amdgpu_waves_per_eu
   // buffer resources over rows t TK .. min(N, (t + 1) TK) - 1 of K and V (bytes past read as 0;
   // none for tiles past N, whose loads then only write zeros to a stage nothing reads again)
   auto tile_rsrc2 = [&](int t, i32x4v& rk, i32x4v& rv) __attribute__((always_inline)) {
-    const int row0 = t * TK;
-    const int rows = min(N - row0, TK);
+    // (DESC: the tiles "after" tile 0 have negative numbers: empty resources, no memory touched)
+    const int row0 = DESC && t < 0 ? 0 : t * TK;
+    const int rows = DESC && t < 0 ? 0 : min(N - row0, TK);
     const unsigned long long off = (unsigned long long)row0 * (unsigned long long)rs;
     const unsigned long long bk = reinterpret_cast<unsigned long long>(kh) + off;
     const unsigned long long bv = reinterpret_cast<unsigned long long>(vh) + off;
@@ -364,52 +405,79 @@ __global__ __launch_bounds__(kWideWaves * 64) __attribute__((amdgpu_waves_per_eu
     for (int dk = 0; dk < DK; dk++) kf[dk] = tile_row_at<D>(tile, lo_, r, dk);
   };
 
-  // prologue: tiles t_lo and t_lo + 1 requested, tile t_lo awaited; S_A(0) shifted and checked
-  issue_tile(t_lo, 0);
-  if (t_lo + 1 < n_tiles) {
-    issue_tile(t_lo + 1, 1);
-    wait_dma_but<2 * WideDma<TK, NS>::PW>();
-  } else {
-    wait_dma();
+  // Tiles past the last key any row of this wave sees (the causal diagonal of its block B, or N)
+  // are fully masked for both blocks and change nothing: the wave only takes part in their barrier
+  // and loads. n_real is wave-uniform; every wave still meets one barrier per tile.
+  const int last_seen = min(N - 1, CAUSAL ? rb + 31 : N - 1);
+  const int n_real = min(n_tiles, last_seen / TK + 1);
+
+  // prologue: the first two tiles requested, the first awaited. In key order tile t sits in stage
+  // (t - t_lo) % 2; from the diagonal down (tiles n_tiles - 1 .. 0) tile t sits in stage t % 2.
+  {
+    const int t0 = DESC ? n_tiles - 1 : t_lo;
+    const bool two = DESC ? t0 >= 1 : t0 + 1 < n_tiles;
+    // (the pieces' LDS addresses are scalar operands: one branch per stage)
+    auto issue_in = [&](int t, int st) __attribute__((always_inline)) {
+      if (st) issue_tile(t, 1);
+      else issue_tile(t, 0);
+    };
+    if constexpr (DESC) issue_in(t0, t0 & 1);
+    else issue_tile(t0, 0);
+    if (two) {
+      if constexpr (DESC) issue_in(t0 - 1, (t0 - 1) & 1);
+      else issue_tile(t0 + 1, 1);
+      wait_dma_but<2 * WideDma<TK, NS>::PW>();
+    } else {
+      wait_dma();
+    }
   }
   race_check_drain();
   __syncthreads();
-  load_k(sK[0], 0);
+  // S_A of the wave's first step (key order: the first step of tile t_lo, in stage 0; from the
+  // diagonal down: the last step of its last real tile), shifted and checked
+  auto first_step = [&](int st, int k0) __attribute__((always_inline)) {
+    const int r0 = DESC ? 32 * (SPT - 1) : 0;
+    load_k(sK[st], r0);
+    auto& v0 = DESC && (SPT - 1) % 2 ? vf2 : vf;  // the V fragment set of that step's parity
 #pragma unroll
-  for (int i = 0; i < 8; i++) vf[i & 3][i >> 2] = tile_tr_at<D>(sV[0], lo_, 16 * (i >> 2), i & 3);
-  {
-    f32x16 s0 = f32x16{};
+    for (int i = 0; i < 8; i++) v0[i & 3][i >> 2] = tile_tr_at<D>(sV[st], lo_, r0 + 16 * (i >> 2), i & 3);
+    f32x16 s0 = ALIBI ? aini : f32x16{};
 #pragma unroll
     for (int dk = 0; dk < DK; dk++) s0 = __builtin_amdgcn_mfma_f32_32x32x16_bf16(kf[dk], A.q[dk], s0, 0, 0, 0);
+    const float ya = ALIBI ? yadd(A, k0, ra) : -A.ref;
 #pragma unroll
-    for (int i = 0; i < 16; i++) A.x[i] = __builtin_fmaf(s0[i], sl2, -A.ref);
+    for (int i = 0; i < 16; i++) A.x[i] = __builtin_fmaf(s0[i], sl2, ya);
     A.xmax = wide_max16(A.x);
-  }
-  if (t_lo * TK + 31 > edgeA || (WINDOW && t_lo * TK < ledgeA))
-    wide_mask<WINDOW>(A, t_lo * TK, lastA, firstA, h);
-  wide_check(A);
+    if (k0 + 31 > edgeA || (WINDOW && k0 < ledgeA)) wide_mask<WINDOW>(A, k0, lastA, firstA, h);
+    wide_check(A);
+  };
+  if constexpr (!DESC) first_step(0, t_lo * TK);
 
   // Step j (sub-step sb of tile t, in stage st): the four phases of the header comment.
   auto step = [&](auto st_c, auto sb_c, int t) __attribute__((always_inline)) {
     constexpr int st = decltype(st_c)::value, sb = decltype(sb_c)::value;
     const int k0 = t * TK + 32 * sb;
-    constexpr bool LAST = sb == SPT - 1;  // last step of tile t
+    const int kn = DESC ? k0 - 32 : k0 + 32;        // first key of step j + 1
+    constexpr bool LAST = sb == (DESC ? 0 : SPT - 1);  // last step of tile t
+    constexpr int rn = DESC ? 32 * (sb - 1) : 32 * (sb + 1);  // rows of step j + 1 in tile t
+    constexpr int rn1 = DESC ? 32 * (SPT - 1) : 0;             // and in the tile after t
     auto& vcur = (sb & 1) ? vf2 : vf;
     auto& vnext = (sb & 1) ? vf : vf2;
     // P1: S_B(j) = K(j) Q_B^T; probabilities of A, step j
-    phase_exp(B, kf, A, [](int) {});
+    phase_exp<ALIBI>(B, kf, A, aini, [](int) {});
     i32x4v rk, rv;
     if constexpr (LAST) {
-      // tile t + 1 in LDS for every wave (each waits for its own pieces, then the barrier)
+      // the next tile in LDS for every wave (each waits for its own pieces, then the barrier)
       wait_dma();
       __syncthreads();  // also: every wave's reads of tile t, whose stage is refilled below, done
-      tile_rsrc2(t + 2, rk, rv);
+      tile_rsrc2(DESC ? t - 2 : t + 2, rk, rv);
     }
-    // P2: K(j+1) requested (and, in a tile's last step, the DMA of tile t + 2); O_A += V(j)^T
-    // P_A(j)^T, A's sum; B's scores shifted and checked
-    phase_pv(A, vcur, B, sl2, [&](int i) __attribute__((always_inline)) {
-      kf[i] = sb < SPT - 1 ? tile_row_at<D>(sK[st], lo_, 32 * (sb + 1), i)
-                           : tile_row_at<D>(sK[st ^ 1], lo_, 0, i);
+    // P2: K(j+1) requested (and, in a tile's last step, the DMA of the tile after the next); O_A
+    // += V(j)^T P_A(j)^T, A's sum; B's scores shifted and checked
+    const float yb = yadd(B, k0, rb);
+    phase_pv<ALIBI>(A, vcur, B, sl2, yb, [&](int i) __attribute__((always_inline)) {
+      if constexpr (LAST) kf[i] = tile_row_at<D>(sK[st ^ 1], lo_, rn1, i);
+      else kf[i] = tile_row_at<D>(sK[st], lo_, rn, i);
       if constexpr (LAST) {
         constexpr int PW = WideDma<TK, NS>::PW, PG = 2 * PW / 8;  // pieces per group
 #pragma unroll
@@ -425,57 +493,85 @@ __global__ __launch_bounds__(kWideWaves * 64) __attribute__((amdgpu_waves_per_eu
       wide_mask<WINDOW>(B, k0, lastB, firstB, h);
     wide_check(B);
     // P3: S_A(j+1) = K(j+1) Q_A^T; probabilities of B, step j
-    phase_exp(A, kf, B, [](int) {});
+    phase_exp<ALIBI>(A, kf, B, aini, [](int) {});
     // P4: O_B += V(j)^T P_B(j)^T, B's sum; A's scores of step j + 1 shifted and checked (past the
     // last step: garbage, fully masked)
-    phase_pv(B, vcur, A, sl2, [&](int i) __attribute__((always_inline)) {
-      // V(j+1): the next step of this tile, or the first of tile t + 1 (visible since this step's
-      // barrier; past the last tile the reads see a stage nothing uses)
-      vnext[i & 3][i >> 2] = LAST ? tile_tr_at<D>(sV[st ^ 1], lo_, 16 * (i >> 2), i & 3)
-                                  : tile_tr_at<D>(sV[st], lo_, 32 * (sb + 1) + 16 * (i >> 2), i & 3);
+    const float ya = yadd(A, kn, ra);
+    phase_pv<ALIBI>(B, vcur, A, sl2, ya, [&](int i) __attribute__((always_inline)) {
+      // V(j+1): the next step of this tile, or the first of the next tile (visible since this
+      // step's barrier; past the last tile the reads see a stage nothing uses)
+      if constexpr (LAST) vnext[i & 3][i >> 2] = tile_tr_at<D>(sV[st ^ 1], lo_, rn1 + 16 * (i >> 2), i & 3);
+      else vnext[i & 3][i >> 2] = tile_tr_at<D>(sV[st], lo_, rn + 16 * (i >> 2), i & 3);
     });
-    if (__builtin_expect(k0 + 63 > edgeA || (WINDOW && k0 + 32 < ledgeA), 0))
-      wide_mask<WINDOW>(A, k0 + 32, lastA, firstA, h);
+    if (__builtin_expect(kn + 31 > edgeA || (WINDOW && kn < ledgeA), 0))
+      wide_mask<WINDOW>(A, kn, lastA, firstA, h);
+    // from the diagonal down, the step after a block's last (keys -32 .. -1, read from a stage of
+    // zeros) is not past the diagonal: hidden here
+    if constexpr (DESC && LAST)
+      if (t == 0) wide_mask_all(A);
     wide_check(A);
   };
   auto run_tile = [&](auto st_c, int tt) __attribute__((always_inline)) {
     auto one = [&](auto sb_c) __attribute__((always_inline)) { step(st_c, sb_c, tt); };
-    one(std::integral_constant<int, 0>{});
-    one(std::integral_constant<int, 1>{});
-    if constexpr (SPT == 4) {
-      one(std::integral_constant<int, 2>{});
-      one(std::integral_constant<int, 3>{});
+    if constexpr (DESC) {
+      if constexpr (SPT == 4) {
+        one(std::integral_constant<int, 3>{});
+        one(std::integral_constant<int, 2>{});
+      }
+      one(std::integral_constant<int, 1>{});
+      one(std::integral_constant<int, 0>{});
+    } else {
+      one(std::integral_constant<int, 0>{});
+      one(std::integral_constant<int, 1>{});
+      if constexpr (SPT == 4) {
+        one(std::integral_constant<int, 2>{});
+        one(std::integral_constant<int, 3>{});
+      }
     }
   };
-  // Tiles past the last key any row of this wave sees (the causal diagonal of its block B, or N)
-  // are fully masked for both blocks and change nothing: the wave only takes part in their barrier
-  // and loads. n_real is wave-uniform; every wave still meets one barrier per tile.
-  const int last_seen = min(N - 1, CAUSAL ? rb + 31 : N - 1);
-  const int n_real = min(n_tiles, last_seen / TK + 1);
   auto idle_tile = [&](auto st_c, int tt) __attribute__((always_inline)) {
     constexpr int st = decltype(st_c)::value;
     wait_dma();
     __syncthreads();
     i32x4v rk, rv;
-    tile_rsrc2(tt + 2, rk, rv);
+    tile_rsrc2(DESC ? tt - 2 : tt + 2, rk, rv);
 #pragma unroll
     for (int i = 0; i < WideDma<TK, NS>::PW; i++) dma.piece(st, 0, i, rk);
 #pragma unroll
     for (int i = 0; i < WideDma<TK, NS>::PW; i++) dma.piece(st, 1, i, rv);
     race_check_drain();
   };
-  int t = t_lo;  // tile t sits in stage (t - t_lo) % 2
-  for (; t + 1 < n_real; t += 2) {
-    run_tile(std::integral_constant<int, 0>{}, t);
-    run_tile(std::integral_constant<int, 1>{}, t + 1);
-  }
-  if (t < n_real) {
-    run_tile(std::integral_constant<int, 0>{}, t);
-    t++;
-  }
-  for (; t < n_tiles; t++) {
-    if ((t - t_lo) & 1) idle_tile(std::integral_constant<int, 1>{}, t);
-    else idle_tile(std::integral_constant<int, 0>{}, t);
+  if constexpr (DESC) {
+    // tiles n_tiles - 1 .. n_real: idle; then the real ones down to tile 0 (in stage 0), in pairs
+    // from the bottom
+    int t = n_tiles - 1;
+    for (; t >= n_real; t--) {
+      if (t & 1) idle_tile(std::integral_constant<int, 1>{}, t);
+      else idle_tile(std::integral_constant<int, 0>{}, t);
+    }
+    first_step(t & 1, t * TK + 32 * (SPT - 1));
+    if ((t & 1) == 0) {
+      run_tile(std::integral_constant<int, 0>{}, t);
+      t--;
+    }
+    for (; t >= 1; t -= 2) {
+      run_tile(std::integral_constant<int, 1>{}, t);
+      run_tile(std::integral_constant<int, 0>{}, t - 1);
+    }
+  } else {
+    int t = t_lo;  // tile t sits in stage (t - t_lo) % 2
+    for (; t + 1 < n_real; t += 2) {
+      run_tile(std::integral_constant<int, 0>{}, t);
+      run_tile(std::integral_constant<int, 1>{}, t + 1);
+    }
+    if (t < n_real) {
+      run_tile(std::integral_constant<int, 0>{}, t);
+      t++;
+    }
+    for (; t < n_tiles; t++) {
+      if ((t - t_lo) & 1) idle_tile(std::integral_constant<int, 1>{}, t);
+      else idle_tile(std::integral_constant<int, 0>{}, t);
+    }
   }
 
   // epilogue: O = a / l, LSE = ln 2 (m + log2 l). O goes out through LDS, whose K/V stages are

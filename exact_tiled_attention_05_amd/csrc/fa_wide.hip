@@ -14,9 +14,11 @@ __attribute__((visibility("hidden"))) hipError_t launch_wide(const WideArgs& arg
   WideArgs a = args;
   void* argv[] = {&a};
   const bool window = causal && a.wl < kWideNoWindow;
-  const void* fn = window ? reinterpret_cast<const void*>(&fa_fwd_wide_kernel<true, true>)
-                 : causal ? reinterpret_cast<const void*>(&fa_fwd_wide_kernel<true, false>)
-                          : reinterpret_cast<const void*>(&fa_fwd_wide_kernel<false, false>);
+  const bool alibi = causal && !window && a.slopes != nullptr;
+  const void* fn = alibi    ? reinterpret_cast<const void*>(&fa_fwd_wide_kernel<true, false, true>)
+                 : window ? reinterpret_cast<const void*>(&fa_fwd_wide_kernel<true, true, false>)
+                 : causal ? reinterpret_cast<const void*>(&fa_fwd_wide_kernel<true, false, false>)
+                          : reinterpret_cast<const void*>(&fa_fwd_wide_kernel<false, false, false>);
   return hipLaunchKernel(fn, dim3(a.n_qblk * a.BH), dim3(kWideWaves * 64), argv, 0, stream);
 }
 

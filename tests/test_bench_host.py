@@ -12,9 +12,9 @@ from exact_tiled_attention_05_amd import workloads as W  # noqa: E402
 
 
 def test_family_follows_the_forward_kernel_choice():
-    # fa_api.hip: the 4-wave kernel for every variant, the wide-row kernel for plain bf16 d = 128
-    # with N >= 4096, the 4-wave kernel for d = 256, the other causal d = 128 grids and grids past
-    # 2^16 rows, the 8-wave kernel for the rest
+    # fa_api.hip: the wide-row kernel for bf16 d = 128 with N >= 4096, plain, with a causal sliding
+    # window or with causal ALiBi; the 4-wave kernel for the other variants, d = 256, the other
+    # causal d = 128 grids and grids past 2^16 rows; the 8-wave kernel for the rest
     assert bench.workload_family("llama3_8b_n8k_causal") == "wide"
     assert bench.workload_family("llama3_8b_gqa_n8k_causal") == "wide"
     assert bench.workload_family("long_n32k_causal") == "wide"
@@ -25,7 +25,7 @@ def test_family_follows_the_forward_kernel_choice():
     assert bench.workload_family("llama3_8b_gqa_decode_b8_n32k") == "decode"
     assert bench.workload_family("llama3_8b_n8k_causal_bwd") == "bwd"
     assert bench.workload_family("b1h16_n4k_bias") == "ext"
-    assert bench.workload_family("llama3_8b_n8k_causal_alibi") == "ext"
+    assert bench.workload_family("llama3_8b_n8k_causal_alibi") == "wide"
     assert bench.device_kernel("single_head_fp32") == "fa_fwd_f32_kernel"
     assert bench.device_kernel("b4h16_n1k_d64").startswith("fa_fwd_bf16_kernel")
     assert bench.device_kernel("llama3_8b_n8k_causal").startswith("fa_fwd_wide_kernel")
