@@ -220,8 +220,9 @@ def run_timed(step, stream, args):
 
 def oracle_pool(tasks, budget_s=15.0, ram_bytes_per_task=0):
     """Run the oracle tasks (callables) on a pool of one worker per available core, with BLAS held
-    to one thread per worker, in batches of one task per worker until the budget is spent (at
-    least one batch). Returns (tasks done, seconds, workers)."""
+    to one thread per worker, in batches of one task per worker, going round the list again while
+    time is left, until the budget is spent (at least one batch). Returns (task runs done, seconds,
+    workers)."""
     import concurrent.futures as cf
     try:
         from threadpoolctl import threadpool_limits
@@ -240,8 +241,8 @@ def oracle_pool(tasks, budget_s=15.0, ram_bytes_per_task=0):
     done, t0 = 0, time.perf_counter()
     workers = max(1, min(workers, len(tasks)))
     with limit, cf.ThreadPoolExecutor(max_workers=workers) as ex:
-        while done < len(tasks):
-            batch = tasks[done:done + workers]
+        while True:
+            batch = [tasks[(done + i) % len(tasks)] for i in range(workers)]
             list(ex.map(lambda f: f(), batch))
             done += len(batch)
             if time.perf_counter() - t0 >= budget_s:
@@ -272,14 +273,15 @@ def cpu_baseline(q, k, v, scale, causal, w, n_heads, budget_s=15.0):
     R = N if rows is None else len(rows)
     done, dt, workers = oracle_pool([task(b, h) for b, h in heads], budget_s,
                                     ram_bytes_per_task=3 * R * N * 8)
+    # (done counts head passes: the pool goes round the heads again while the budget lasts)
     if rows is None:
         flops = W.metric_flops(1, done, N, d, causal)
-        what = "%d of %d heads, every row" % (done, B * H)
+        what = "%d passes over %d of %d heads, every row" % (done, len(heads), B * H)
     else:
         per_row = [4 * ((i + 1) if causal else N) * d for i in rows]
         flops = done * float(sum(per_row))
-        what = "%d of %d heads, the %d sampled rows of each (FLOPs 4*(i+1)*d per causal row i)" % (
-            done, B * H, len(rows))
+        what = ("%d passes over %d of %d heads, the %d sampled rows of each (FLOPs 4*(i+1)*d per "
+                "causal row i)" % (done, len(heads), B * H, len(rows)))
     return dict({"value": flops / dt / 1e12, "unit": "TFLOP/s", "cores": workers, "kind": "oracle",
                  "sample": "%s; numpy float64 with dense S and P, one head per worker, BLAS at one "
                            "thread per worker, %.1f s" % (what, dt)}, **host_info())
@@ -354,9 +356,9 @@ def bench_decode(args, w):
         # each (b, h) reads its K/V head once: bytes of the heads done, at the oracle's rate
         rec["cpu_baseline"] = {"value": done * Nkv * d * 2 * 2 / dt / 1e9, "unit": "GB/s",
                                "cores": workers, "kind": "oracle",
-                               "sample": "%d of %d (batch, head) pairs, numpy float64, one pair "
-                                         "per worker, BLAS at one thread per worker, %.1f s"
-                                         % (done, B * H, dt)}
+                               "sample": "%d passes over the %d (batch, head) pairs, numpy "
+                                         "float64, one pair per worker, BLAS at one thread per "
+                                         "worker, %.1f s" % (done, B * H, dt)}
         rec["cpu_baseline"].update(host_info())
     print(json.dumps(rec), flush=True)
 
@@ -436,9 +438,10 @@ def bench_variant(args, w):
         cflops = W.metric_flops_masked(1, done, N, d, causal, win)
         rec["cpu_baseline"] = {"value": cflops / dt / 1e12, "unit": "TFLOP/s", "cores": workers,
                                "kind": "oracle",
-                               "sample": "%d of %d heads of batch 0, every row (numpy float64, "
-                                         "dense S and P), one head per worker, BLAS at one thread "
-                                         "per worker, %.1f s" % (done, B * H, dt)}
+                               "sample": "%d passes over the %d heads of batch 0 (of %d), every "
+                                         "row (numpy float64, dense S and P), one head per worker, "
+                                         "BLAS at one thread per worker, %.1f s"
+                                         % (done, H, B * H, dt)}
         rec["cpu_baseline"].update(host_info())
     print(json.dumps(rec), flush=True)
 
@@ -514,9 +517,10 @@ def bench_backward(args, w):
         cflops = W.metric_flops_bwd(1, done, N, d, causal)
         rec["cpu_baseline"] = {"value": cflops / dt / 1e12, "unit": "TFLOP/s", "cores": workers,
                                "kind": "oracle",
-                               "sample": "%d of %d heads of batch 0, every row (numpy float64, "
-                                         "dense S, P, dP, dS), one head per worker, BLAS at one "
-                                         "thread per worker, %.1f s" % (done, B * H, dt)}
+                               "sample": "%d passes over the %d heads of batch 0 (of %d), every "
+                                         "row (numpy float64, dense S, P, dP, dS), one head per "
+                                         "worker, BLAS at one thread per worker, %.1f s"
+                                         % (done, H, B * H, dt)}
         rec["cpu_baseline"].update(host_info())
     print(json.dumps(rec), flush=True)
 

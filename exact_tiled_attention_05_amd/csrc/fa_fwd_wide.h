@@ -1,6 +1,6 @@
 // Wide-row forward kernel for gfx950, head dim 128: the bench workload (causal Llama-3-8B layer),
-// the other large d = 128 grids, and causal sliding windows on them (the choice is made in
-// fa_api.hip).
+// the other large d = 128 grids, and causal sliding windows or causal ALiBi on them (the choice is
+// made in fa_api.hip).
 //
 // The method is the one of the other forward kernels ("FlashAttention-2 -- Deeper Math", Fixes
 // 1-5 and "Causal masking: skip the blocks"; "Understanding FlashAttention Pt 1", §2.4 and §3.1):
@@ -42,6 +42,11 @@
 //   * With a causal sliding window (row q sees keys q - wl .. q) a workgroup starts at the tile of
 //     its first row's first key; the steps before a block's window are masked like those past its
 //     diagonal (the waves above the first row run through a few fully masked steps first).
+//   * With causal ALiBi the key tiles are walked from the diagonal down (tile n_tiles - 1 first,
+//     the steps of a tile from its last to its first, tile t in stage t % 2): the ALiBi term falls
+//     away from the diagonal, so the first steps set the lazy reference and it seldom moves again.
+//     The waves whose diagonal lies below the workgroup's last tile meet those tiles' barriers
+//     first, and each block's step after its last one (keys below 0) is hidden.
 //   * Every wave takes part in every tile of its workgroup's key range, so the barrier counts
 //     match. The steps past a block's causal diagonal (or past N) are fully masked, which makes
 //     their probabilities 0 and leaves the running state unchanged; once a whole tile is past both

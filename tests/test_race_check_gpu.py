@@ -93,8 +93,9 @@ def test_forward_matches_race_check_build(race_lib, name, w):
 
 
 def test_variants_match_race_check_build(race_lib):
-    """Sliding window with grouped heads, ALiBi, and an additive bias (its own LDS tiles, loaded
-    ahead of the K/V tiles they belong to)."""
+    """Sliding window with grouped heads and causal ALiBi (both on the wide-row kernel at N = 8192,
+    ALiBi walking the key tiles from the diagonal down), and an additive bias (its own LDS tiles,
+    loaded ahead of the K/V tiles they belong to)."""
     B, H, H_kv, N, d = 1, 8, 2, 8192, 128
     q, k, v = make_inputs(B=B, H=H, H_kv=H_kv, N=N, d=d, dtype="bf16", seed=5)
     qd, kd, vd = (to_layout(x, "bnhd").to(DEV) for x in (q, k, v))
