@@ -121,12 +121,14 @@ def test_window_long_causal(B, N, H, H_kv, layout, window):
 @pytest.mark.parametrize("B,N,H,H_kv,layout,slope_mult,scale_mult", [
     (1, 4096, 4, 4, "bhnd", 1.0, 1.0), (2, 4097, 4, 2, "bnhd", 1.0, 1.0),
     (1, 5000, 2, 1, "bnhd", 64.0, 1.0), (1, 4160, 2, 2, "bhnd", 0.25, 0.05),
-    (1, 8192, 4, 1, "bnhd", 1.0, 1.0), (1, 4096, 2, 1, "bhnd", 1.0, 1e-5)])
+    (1, 8192, 4, 1, "bnhd", 1.0, 1.0), (1, 4096, 2, 1, "bhnd", 1.0, 1e-5),
+    (1, 32768, 2, 2, "bhnd", 1.0, 1.0)])
 def test_alibi_long_causal(B, N, H, H_kv, layout, slope_mult, scale_mult):
     """Causal ALiBi at d = 128 and N >= 4096 (on the wide-row kernel, walking the keys from the
     diagonal down): ragged lengths, grouped heads, both layouts, slopes up to 64x the geometric
-    ones (a strongly local softmax), a small scale, and a scale below 1e-6 (left to the 4-wave
-    kernel), on sampled rows plus the first and last 70 rows."""
+    ones (a strongly local softmax), a small scale, a scale below 1e-6 (left to the 4-wave
+    kernel) and N = 32768 (rows far from key 0, where the ALiBi term is large), on sampled rows
+    plus the first and last 70 rows."""
     q, k, v = make_inputs(B, H, N, 128, H_kv=H_kv, seed=N + H)
     rows = np.unique(np.concatenate([sampled_rows(N, 96, seed=N).numpy(),
                                      np.arange(0, 70), np.arange(N - 70, N)]))
