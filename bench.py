@@ -619,7 +619,7 @@ def recorded_traffic(workload):
 def main():
     args = parse()
     if args.gpus != 1:
-        print("bench.py: this build runs on exactly one GPU (no multi-GPU path); "
+        print("bench.py: the library runs on one GPU only (no multi-GPU path); "
               "run with --gpus 1", file=sys.stderr)
         sys.exit(2)
 

@@ -16,11 +16,11 @@ typedef float f32x16 __attribute__((ext_vector_type(16)));
 // Race-check build (compiled with -DFA_RACE_CHECK=1). The kernels overlap the loads of the next
 // K/V tiles into LDS with the products on the current ones; a missing wait or barrier there would
 // let a wave read a tile before it has landed, or let a load overwrite a tile a wave still reads.
-// In this build every tile load completes, for every wave of the work-group, before any wave goes
-// on (a full wait and a barrier right after the loads are issued, a barrier before a staged store),
-// and LDS starts filled with all-ones bytes (NaN as bf16 and as fp32). The arithmetic and its order
-// are unchanged, so a race-free fast build gives bit-identical outputs; a race shows as a
-// difference, and a read of LDS that no load wrote shows as NaN.
+// In the race-check build every tile load completes, for every wave of the work-group, before
+// any wave goes on (a full wait and a barrier right after the loads are issued, a barrier before a
+// staged store), and LDS starts filled with all-ones bytes (NaN as bf16 and as fp32). The
+// arithmetic and its order are unchanged, so a race-free fast build gives bit-identical outputs;
+// a race shows as a difference, and a read of LDS that no load wrote shows as NaN.
 #ifndef FA_RACE_CHECK
 #define FA_RACE_CHECK 0
 #endif
